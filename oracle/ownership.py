@@ -1,0 +1,109 @@
+"""Checks of a per-tile ownership log against the schedulers' ownership rules.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+A log holds one record per tile id: the worker (launch slot index) that ran it,
+its start/end timestamps, and a visit count incremented atomically each time
+any worker finished that tile. The rules:
+
+* Every mode: each unit of work has exactly one owner ([CLC], section
+  "cancelling the launch, receiving the work coordinate": the same coordinate
+  never appears in two successful responses, so work either runs in its own
+  launch or is taken by exactly one running worker). So visits == 1 for every
+  tile handed out, 0 for every other, and a worker's tiles never overlap in time
+  (a running block is never taken over, same section).
+* Non-persistent: owner(k) = k (one block per tile; [CLC], section "from one
+  tile per block ...", three-mode table).
+* Static: owner(k) = k mod P and each worker's tiles run in increasing order
+  ([CLC], section "why a fixed task sequence tails": W_i = i, i+4, i+8 for P = 4).
+* Dynamic: any exactly-once owner map is valid (the claim order decides it);
+  because claims come from one monotone counter each worker's tiles are
+  strictly increasing in both id and start time.
+
+Timestamps are taken on the GPU's constant-rate clock; makespan = latest tile
+end - earliest tile start over the tiles that ran.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Iterable, List, Optional
+
+import numpy as np
+
+__all__ = ["check_ownership", "makespan", "per_worker"]
+
+
+def per_worker(worker: np.ndarray, tiles: np.ndarray) -> Dict[int, np.ndarray]:
+    out: Dict[int, List[int]] = {}
+    for w, k in zip(worker.tolist(), tiles.tolist()):
+        out.setdefault(int(w), []).append(int(k))
+    return {w: np.asarray(v, dtype=np.int64) for w, v in out.items()}
+
+
+def makespan(start: np.ndarray, end: np.ndarray) -> float:
+    if len(start) == 0:
+        return 0.0
+    return float(np.max(end) - np.min(start))
+
+
+def check_ownership(mode: str, T: int, tile: np.ndarray, worker: np.ndarray, start: np.ndarray,
+                    end: np.ndarray, visits: np.ndarray, P: Optional[int] = None,
+                    expected_tiles: Optional[Iterable[int]] = None) -> List[str]:
+    """Return a list of violations (empty when the log obeys every rule).
+
+    ``tile``, ``worker``, ``start``, ``end`` are per-record arrays for the tiles that
+    ran (records of tiles that never ran must be dropped by the caller, using
+    ``visits == 0``); ``visits`` is the full per-tile visit array of length T.
+    ``expected_tiles`` is the set of tile ids that must have run (default all).
+    """
+    errs: List[str] = []
+    tile = np.asarray(tile, dtype=np.int64)
+    worker = np.asarray(worker, dtype=np.int64)
+    start = np.asarray(start, dtype=np.float64)
+    end = np.asarray(end, dtype=np.float64)
+    visits = np.asarray(visits, dtype=np.int64)
+    if len(visits) != T:
+        errs.append(f"visits has length {len(visits)}, expected {T}")
+        return errs
+    expected = np.zeros(T, dtype=np.int64)
+    if expected_tiles is None:
+        expected[:] = 1
+    else:
+        for k in expected_tiles:
+            expected[int(k)] = 1
+    bad = np.nonzero(visits != expected)[0]
+    if len(bad):
+        errs.append(f"visit counts differ from exactly-once at {len(bad)} tiles, first {bad[:8].tolist()} "
+                    f"(visits {visits[bad[:8]].tolist()})")
+    ran = sorted(tile.tolist())
+    want = sorted(np.nonzero(expected)[0].tolist())
+    if ran != want:
+        errs.append(f"logged tile set differs from expected ({len(ran)} logged, {len(want)} expected)")
+    if np.any(end < start):
+        errs.append("a tile ends before it starts")
+    groups: Dict[int, List[int]] = {}
+    for i, w in enumerate(worker.tolist()):
+        groups.setdefault(int(w), []).append(i)
+    for w, idx in groups.items():
+        idx = sorted(idx, key=lambda i: (start[i], tile[i]))
+        ks = tile[idx]
+        st = start[idx]
+        en = end[idx]
+        if len(idx) > 1 and np.any(st[1:] < en[:-1]):
+            errs.append(f"worker {w} runs two tiles at once")
+        if mode in ("static", "dynamic") and len(ks) > 1 and np.any(np.diff(ks) <= 0):
+            errs.append(f"worker {w} tiles not increasing in start order: {ks[:8].tolist()}")
+    if mode == "nonpersistent":
+        if np.any(worker != tile):
+            errs.append("non-persistent owner(k) != k")
+        for w, idx in groups.items():
+            if len(idx) != 1:
+                errs.append(f"non-persistent worker {w} ran {len(idx)} tiles")
+    elif mode == "static":
+        if P is None or P < 1:
+            errs.append("static check needs P")
+        elif np.any(worker != tile % P):
+            errs.append("static owner(k) != k mod P")
+    elif mode != "dynamic":
+        errs.append(f"unknown mode {mode}")
+    return errs
