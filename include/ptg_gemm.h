@@ -1,0 +1,210 @@
+/*
+ * ptg_gemm.h - C ABI of the persistent tiled bf16 GEMM for MI355X (gfx950).
+ *
+ * Operation. C[m][n] = sum_k A[m][k] * B[k][n] with A, B in bf16 and C in fp32
+ * (fp32 accumulation, C overwritten). The output is cut into BM x BN tiles;
+ * each tile is one unit of work over the whole K extent, computed exactly once
+ * by one worker (a workgroup). Sources: "CUTLASS Cluster Launch Control dynamic
+ * persistent kernel" (blog post), section "from one tile per block to one
+ * worker computing continuously" (a unit is one full output tile, no split-K)
+ * and section "cancelling the launch, receiving the work coordinate" (each
+ * unit has exactly one owner).
+ *
+ * Schedulers (same blog post, the three-mode table in the first section):
+ *   GEMM_SCHED_NONPERSISTENT  grid = all tiles; block b computes tile b and exits.
+ *   GEMM_SCHED_STATIC         grid = P workers; worker i computes i, i+P, i+2P, ...
+ *                             (section "why a fixed task sequence tails").
+ *   GEMM_SCHED_DYNAMIC        grid = all tiles (launch slots); every workgroup takes
+ *                             tiles from one device-wide atomic claim counter, the
+ *                             claim of the next tile is prefetched through a ring of
+ *                             response records in LDS (depth 3), a failed claim ends
+ *                             the worker, late-launched slots exit after one failed
+ *                             claim. This replaces the hardware launch-cancel of the
+ *                             blog post (sections "cancelling the launch ..." and
+ *                             "following the CUTLASS source"), which gfx950 lacks.
+ *
+ * Layouts. Row-major and contiguous: A is M x K (lda = K), B is K x N (ldb = N),
+ * C is M x N (ldc = N). bf16 is passed as raw 16-bit patterns. Device pointers
+ * only (hipMalloc / torch device memory). A, B and C must be 16-byte aligned;
+ * K and N must be multiples of 8 (16-byte rows); M is arbitrary. Edge tiles
+ * (M, N, K not multiples of the tile) are handled by masking.
+ *
+ * Ownership. The caller owns A, B, C and keeps them alive until the stream has
+ * passed the kernel. The plan (gemm_tile_cfg) owns all library scratch: the
+ * claim counter, the tile log, the visit counters and the grouped-problem table.
+ * Runs are asynchronous and stream-ordered; nothing here synchronises except
+ * gemm_read_log and gemm_spoiler_run's optional residency wait. A plan serves
+ * one stream at a time and is not thread-safe.
+ *
+ * Errors. Every call returns a gemm_status; 0 is success. Invalid arguments are
+ * rejected before anything is enqueued. HIP failures return GEMM_E_HIP and the
+ * HIP error text is kept in the plan (gemm_last_hip_error). Nothing aborts and
+ * nothing throws across this boundary.
+ */
+#ifndef PTG_GEMM_H
+#define PTG_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gemm_status {
+  GEMM_OK = 0,
+  GEMM_E_INVALID_ARG = -1, /* null pointer, bad enum, bad descriptor field */
+  GEMM_E_SHAPE = -2,       /* negative size, K or N not a multiple of 8, over a size limit */
+  GEMM_E_UNSUPPORTED = -3, /* device is not gfx950, or an unsupported tile shape */
+  GEMM_E_DEVICE = -4,      /* plan used while another device is current */
+  GEMM_E_HIP = -5,         /* a HIP runtime call failed (see gemm_last_hip_error) */
+  GEMM_E_NOMEM = -6,       /* device or pinned allocation failed */
+  GEMM_E_TIMEOUT = -7,     /* a bounded wait ran out (spoiler residency, concurrency gate) */
+  GEMM_E_SCHED = -8        /* the kernel flagged a claim-ring protocol violation */
+} gemm_status;
+
+typedef enum gemm_sched_mode {
+  GEMM_SCHED_NONPERSISTENT = 0,
+  GEMM_SCHED_STATIC = 1,
+  GEMM_SCHED_DYNAMIC = 2
+} gemm_sched_mode;
+
+/* Size limits (checked; GEMM_E_SHAPE beyond them). */
+#define GEMM_MAX_K (1 << 20)
+#define GEMM_MAX_N (1 << 22)
+#define GEMM_MAX_M (1 << 30)
+#define GEMM_MAX_TILES (1 << 30)
+
+/*
+ * Plan descriptor (a value type; gemm_create copies it). Fields:
+ *   bm, bn, bk      output tile and K step: {128,128,64} or {256,256,64}.
+ *   ring_depth      depth of the LDS ring of claim records: 3 (2..3 accepted).
+ *   claims_ahead    throttle: how many claims a dynamic worker holds beyond its
+ *                   current tile: 0 (claim after finishing), 1 (claim when a tile
+ *                   starts) or 2; must be < ring_depth.
+ *   raster          0 = row-major tile order; 1 = grouped-M with group height
+ *                   raster_group tile rows.
+ *   static_workers  static mode's P; 0 = resident workgroups (occupancy x CUs).
+ *   log_capacity    tiles to log per run; 0 turns the tile log off.
+ *   min_lds_bytes   dynamic LDS padding per workgroup (limits residency; 0 = none).
+ *   max_concurrent  0 = no cap; n > 0 lets at most n workgroups compute at once
+ *                   (a device-side gate with a bounded wait).
+ *   max_groups      capacity of the grouped-problem table (0 = 1024).
+ *   device          HIP device ordinal; must be gfx950.
+ */
+typedef struct gemm_tile_desc {
+  int32_t bm, bn, bk;
+  int32_t ring_depth;
+  int32_t claims_ahead;
+  int32_t raster;
+  int32_t raster_group;
+  int32_t static_workers;
+  int32_t log_capacity;
+  int32_t min_lds_bytes;
+  int32_t max_concurrent;
+  int32_t max_groups;
+  int32_t device;
+} gemm_tile_desc;
+
+/* Opaque plan: the tile_cfg argument of gemm_run. Owns all library scratch. */
+typedef struct gemm_plan *gemm_tile_cfg;
+
+/*
+ * One tile-log record (host copy). tile: tile id in raster order (grouped: ids
+ * of problem g follow those of problems < g); worker: launch slot (blockIdx.x)
+ * that ran it; hw_id / xcc_id: raw HW_ID and XCC_ID hardware registers of the
+ * wave that ran it; t0/t1: s_memtime at tile start / after its stores were
+ * issued; r0/r1: the same moments on the constant-rate s_memrealtime clock
+ * (rate: gemm_plan_info's wallclock_khz); visits: how many times the tile was
+ * finished (exactly-once => 1); problem: grouped problem index (0 otherwise).
+ */
+typedef struct gemm_tile_rec {
+  uint32_t tile, worker, hw_id, xcc_id;
+  uint64_t t0, t1, r0, r1;
+  uint32_t visits, problem;
+} gemm_tile_rec;
+
+/* Facts about a plan and its last run. */
+typedef struct gemm_plan_info {
+  int32_t device;
+  int32_t cu_count;          /* compute units */
+  int32_t occupancy;         /* resident workgroups per CU for this plan's kernel */
+  int32_t static_workers;    /* P the static mode uses for a large problem */
+  int64_t wallclock_khz;     /* s_memrealtime rate */
+  int64_t last_tiles;        /* T of the last run */
+  int64_t last_grid;         /* grid size of the last run */
+  int32_t last_mode;         /* scheduler of the last run (-1 before the first) */
+  int32_t lds_bytes;         /* LDS per workgroup */
+} gemm_plan_info;
+
+/* Fill *out with the defaults for a square tile edge of 128 or 256 on `device`. */
+gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t device);
+
+/* Validate *desc and build a plan on desc->device. *out receives the plan. */
+gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc);
+
+/*
+ * Enqueue C = A.B on `stream` (a hipStream_t; NULL = the null stream) with
+ * scheduler `sched_mode`. A: M x K bf16, B: K x N bf16, C: M x N fp32, all
+ * device pointers. M == 0 or N == 0 enqueues nothing; K == 0 writes zeros.
+ */
+gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t N, int64_t K,
+                     int32_t sched_mode, gemm_tile_cfg tile_cfg, void *stream);
+
+/*
+ * Grouped variant: G independent problems C_g = A_g.B_g in one launch, their
+ * tiles numbered problem after problem. A, B, C, M, N, K are host arrays of
+ * length G (copied before return; the caller may free them). Each problem
+ * follows the single-GEMM rules. G <= the plan's max_groups.
+ */
+gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const *B, float *const *C,
+                             const int64_t *M, const int64_t *N, const int64_t *K,
+                             int32_t sched_mode, gemm_tile_cfg tile_cfg, void *stream);
+
+/*
+ * Synchronise the last run's stream and copy its tile log to host_out (up to
+ * cap records, in tile-id order, including tiles that never ran: visits == 0).
+ * *n_out receives the number of records written. Returns GEMM_E_TIMEOUT if a
+ * workgroup of the run gave up waiting at the concurrency gate, GEMM_E_SCHED if
+ * a consumer found a ring record for the wrong ordinal (the log is still copied).
+ */
+gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_t cap, size_t *n_out);
+
+/* Read plan facts. */
+gemm_status gemm_plan_info_get(gemm_tile_cfg tile_cfg, gemm_plan_info *out);
+
+/* Release the plan and its scratch (synchronises its last stream first). NULL is a no-op. */
+gemm_status gemm_destroy(gemm_tile_cfg tile_cfg);
+
+/* Static text for a status code. */
+const char *gemm_status_str(int32_t status);
+
+/* Text of the last HIP error seen by this plan ("" if none). */
+const char *gemm_last_hip_error(gemm_tile_cfg tile_cfg);
+
+/*
+ * Failure forcing for tests: the next dynamic run starts its claim counter at
+ * `start` instead of 0, so exactly tiles start..T-1 are computed and every
+ * worker's claims fail once the counter passes T-1 (a claim fails when no work
+ * is left: blog post, section "cluster granularity and exit after failure").
+ */
+gemm_status gemm_test_preset_counter(gemm_tile_cfg tile_cfg, uint32_t start);
+
+/*
+ * Occupy `n_wgs` compute units for `spin_ns` nanoseconds on `stream`: each
+ * workgroup takes a whole CU's LDS, records {s_memrealtime at start, HW_ID,
+ * XCC_ID, end} into d_log (4 uint64 per workgroup; may be NULL) and spins on the
+ * constant-rate clock until its time is up (a bounded wait). This is the
+ * "some SMs are occupied by another kernel" scenario of the blog post's section
+ * "why a fixed task sequence tails". If wait_resident_ms > 0 the call returns
+ * only once all n_wgs workgroups have started, or GEMM_E_TIMEOUT after that
+ * many milliseconds (the spoiler still ends on its own).
+ */
+gemm_status gemm_spoiler_run(int32_t device, int32_t n_wgs, int64_t spin_ns, void *stream,
+                             uint64_t *d_log, double wait_resident_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTG_GEMM_H */

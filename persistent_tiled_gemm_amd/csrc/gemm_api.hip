@@ -1,0 +1,462 @@
+// Host side of the C ABI declared in include/ptg_gemm.h: plan creation and
+// validation, launch sizing per scheduler, per-run scratch reset, tile-log
+// readback, the spoiler and failure-forcing helpers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "ptg_gemm.h"
+#include "ptg_internal.hpp"
+
+using ptg::KernelArgs;
+using ptg::KernelProblem;
+using ptg::SchedCtrl;
+using ptg::TileRecDev;
+
+struct gemm_plan {
+  gemm_tile_desc desc;
+  int cu_count = 0;
+  int occupancy = 0;
+  int static_workers = 0;
+  int64_t wallclock_khz = 0;
+  int lds_bytes = 0;
+  int dyn_lds = 0;
+  // device scratch: [SchedCtrl][visits u32 x log_capacity] in one block, plus the log
+  unsigned char *d_ctrl_block = nullptr;
+  size_t ctrl_block_bytes = 0;
+  TileRecDev *d_log = nullptr;
+  KernelProblem *d_groups = nullptr;
+  KernelProblem *h_groups = nullptr;  // pinned staging for the grouped table
+  hipEvent_t groups_uploaded = nullptr;
+  bool groups_event_pending = false;
+  std::vector<KernelProblem> last_groups;  // what d_groups holds
+  uint32_t preset = 0;
+  bool preset_pending = false;
+  // last run
+  hipStream_t last_stream = nullptr;
+  bool has_run = false;
+  int64_t last_tiles = 0;
+  int64_t last_grid = 0;
+  int32_t last_mode = -1;
+  std::vector<int32_t> last_tile_start;  // per problem (grouped), for log decoding
+  std::string last_error;
+};
+
+namespace {
+
+gemm_status hip_fail(gemm_plan *p, hipError_t e, const char *what) {
+  if (p) {
+    p->last_error = std::string(what) + ": " + hipGetErrorString(e);
+  }
+  return GEMM_E_HIP;
+}
+
+bool valid_tile(const gemm_tile_desc &d) {
+  return (d.bm == 256 && d.bn == 256 && d.bk == 64) || (d.bm == 128 && d.bn == 128 && d.bk == 64);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+gemm_status check_problem(const void *A, const void *B, const float *C, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return GEMM_E_SHAPE;
+  if (M > GEMM_MAX_M || N > GEMM_MAX_N || K > GEMM_MAX_K) return GEMM_E_SHAPE;
+  if ((N % 8) != 0 || (K % 8) != 0) return GEMM_E_SHAPE;
+  if (M == 0 || N == 0) return GEMM_OK;
+  if (C == nullptr) return GEMM_E_INVALID_ARG;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_E_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) | reinterpret_cast<uintptr_t>(C)) & 15u)
+    return GEMM_E_INVALID_ARG;
+  return GEMM_OK;
+}
+
+gemm_status check_current_device(gemm_plan *p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(p, e, "hipGetDevice");
+  if (dev != p->desc.device) return GEMM_E_DEVICE;
+  return GEMM_OK;
+}
+
+// Clear the scheduler state (and the visit counters of the tiles to be logged).
+gemm_status reset_scratch(gemm_plan *p, int64_t tiles, hipStream_t s) {
+  size_t bytes = sizeof(SchedCtrl);
+  if (p->desc.log_capacity > 0) bytes += sizeof(uint32_t) * (size_t)std::min<int64_t>(tiles, p->desc.log_capacity);
+  hipError_t e = hipMemsetAsync(p->d_ctrl_block, 0, bytes, s);
+  if (e != hipSuccess) return hip_fail(p, e, "hipMemsetAsync(scratch)");
+  return GEMM_OK;
+}
+
+gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, int64_t tiles, hipStream_t s) {
+  if (mode < GEMM_SCHED_NONPERSISTENT || mode > GEMM_SCHED_DYNAMIC) return GEMM_E_INVALID_ARG;
+  int64_t grid = tiles;
+  if (mode == GEMM_SCHED_STATIC) grid = std::min<int64_t>(tiles, p->static_workers);
+  args.T = (int32_t)tiles;
+  args.P = (int32_t)grid;
+  args.claims_ahead = p->desc.claims_ahead;
+  args.ring_depth = p->desc.ring_depth;
+  args.raster_group = p->desc.raster == 1 ? p->desc.raster_group : 1;
+  args.counter_base = 0;
+  if (mode == GEMM_SCHED_DYNAMIC && p->preset_pending) {
+    args.counter_base = p->preset;
+    p->preset_pending = false;
+  }
+  args.max_concurrent = p->desc.max_concurrent;
+  args.log_cap = p->desc.log_capacity;
+  args.ctrl = reinterpret_cast<SchedCtrl *>(p->d_ctrl_block);
+  args.visits = reinterpret_cast<uint32_t *>(p->d_ctrl_block + sizeof(SchedCtrl));
+  args.log = p->d_log;
+  gemm_status st = reset_scratch(p, tiles, s);
+  if (st != GEMM_OK) return st;
+  hipError_t e = ptg::launch_gemm(p->desc.bm, mode, grouped, args, (int)grid, p->dyn_lds, s);
+  if (e != hipSuccess) return hip_fail(p, e, "kernel launch");
+  p->last_stream = s;
+  p->has_run = true;
+  p->last_tiles = tiles;
+  p->last_grid = grid;
+  p->last_mode = mode;
+  return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gemm_status_str(int32_t status) {
+  switch (status) {
+    case GEMM_OK: return "ok";
+    case GEMM_E_INVALID_ARG: return "invalid argument";
+    case GEMM_E_SHAPE: return "unsupported shape (negative, K or N not a multiple of 8, or over a size limit)";
+    case GEMM_E_UNSUPPORTED: return "unsupported device or tile configuration (gfx950 only; tiles 128x128x64 or 256x256x64)";
+    case GEMM_E_DEVICE: return "plan used while a different device is current";
+    case GEMM_E_HIP: return "HIP runtime error";
+    case GEMM_E_NOMEM: return "out of memory";
+    case GEMM_E_TIMEOUT: return "timed out waiting";
+    case GEMM_E_SCHED: return "device-side claim-ring protocol violation";
+    default: return "unknown status";
+  }
+}
+
+gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t device) {
+  if (!out) return GEMM_E_INVALID_ARG;
+  if (tile_edge != 128 && tile_edge != 256) return GEMM_E_UNSUPPORTED;
+  std::memset(out, 0, sizeof(*out));
+  out->bm = out->bn = tile_edge;
+  out->bk = 64;
+  out->ring_depth = 3;
+  out->claims_ahead = 1;
+  out->raster = 0;
+  out->raster_group = 8;
+  out->static_workers = 0;
+  out->log_capacity = 0;
+  out->min_lds_bytes = 0;
+  out->max_concurrent = 0;
+  out->max_groups = 1024;
+  out->device = device;
+  return GEMM_OK;
+}
+
+gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
+  if (!out || !desc) return GEMM_E_INVALID_ARG;
+  *out = nullptr;
+  const gemm_tile_desc d = *desc;
+  if (!valid_tile(d)) return GEMM_E_UNSUPPORTED;
+  if (d.ring_depth < 2 || d.ring_depth > 3) return GEMM_E_INVALID_ARG;
+  if (d.claims_ahead < 0 || d.claims_ahead > 2 || d.claims_ahead >= d.ring_depth) return GEMM_E_INVALID_ARG;
+  if (d.raster < 0 || d.raster > 1 || (d.raster == 1 && d.raster_group < 1)) return GEMM_E_INVALID_ARG;
+  if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
+      d.max_groups < 0)
+    return GEMM_E_INVALID_ARG;
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return GEMM_E_HIP;
+  if (d.device < 0 || d.device >= ndev) return GEMM_E_INVALID_ARG;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, d.device);
+  if (e != hipSuccess) return GEMM_E_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_E_UNSUPPORTED;
+  int cur = 0;
+  e = hipGetDevice(&cur);
+  if (e != hipSuccess) return GEMM_E_HIP;
+  if (cur != d.device) return GEMM_E_DEVICE;
+
+  gemm_plan *p = new (std::nothrow) gemm_plan();
+  if (!p) return GEMM_E_NOMEM;
+  p->desc = d;
+  if (p->desc.max_groups == 0) p->desc.max_groups = 1024;
+  p->cu_count = prop.multiProcessorCount;
+  int wclk = 0;
+  if (hipDeviceGetAttribute(&wclk, hipDeviceAttributeWallClockRate, d.device) == hipSuccess) p->wallclock_khz = wclk;
+  const int static_lds = ptg::gemm_static_lds_bytes(d.bm);
+  p->dyn_lds = 0;
+  if (d.min_lds_bytes > static_lds) p->dyn_lds = d.min_lds_bytes - static_lds;
+  p->lds_bytes = static_lds + p->dyn_lds;
+  if (p->lds_bytes > (int)prop.sharedMemPerBlock) {
+    delete p;
+    return GEMM_E_INVALID_ARG;
+  }
+  int occ = 0;
+  e = ptg::gemm_occupancy(d.bm, p->dyn_lds, &occ);
+  if (e != hipSuccess || occ < 1) {
+    delete p;
+    return GEMM_E_HIP;
+  }
+  p->occupancy = occ;
+  p->static_workers = d.static_workers > 0 ? d.static_workers : occ * p->cu_count;
+
+  p->ctrl_block_bytes = sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)std::max(d.log_capacity, 1);
+  if (hipMalloc(&p->d_ctrl_block, p->ctrl_block_bytes) != hipSuccess) {
+    delete p;
+    return GEMM_E_NOMEM;
+  }
+  if (hipMemset(p->d_ctrl_block, 0, p->ctrl_block_bytes) != hipSuccess) {
+    gemm_destroy(p);
+    return GEMM_E_HIP;
+  }
+  if (d.log_capacity > 0) {
+    if (hipMalloc(&p->d_log, sizeof(TileRecDev) * (size_t)d.log_capacity) != hipSuccess) {
+      gemm_destroy(p);
+      return GEMM_E_NOMEM;
+    }
+  }
+  if (hipMalloc(&p->d_groups, sizeof(KernelProblem) * (size_t)p->desc.max_groups) != hipSuccess) {
+    gemm_destroy(p);
+    return GEMM_E_NOMEM;
+  }
+  if (hipHostMalloc(&p->h_groups, sizeof(KernelProblem) * (size_t)p->desc.max_groups, hipHostMallocDefault) !=
+      hipSuccess) {
+    p->h_groups = nullptr;
+    gemm_destroy(p);
+    return GEMM_E_NOMEM;
+  }
+  if (hipEventCreateWithFlags(&p->groups_uploaded, hipEventDisableTiming) != hipSuccess) {
+    p->groups_uploaded = nullptr;
+    gemm_destroy(p);
+    return GEMM_E_HIP;
+  }
+  *out = p;
+  return GEMM_OK;
+}
+
+gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t N, int64_t K, int32_t sched_mode,
+                     gemm_tile_cfg tile_cfg, void *stream) {
+  gemm_plan *p = tile_cfg;
+  if (!p) return GEMM_E_INVALID_ARG;
+  if (sched_mode < GEMM_SCHED_NONPERSISTENT || sched_mode > GEMM_SCHED_DYNAMIC) return GEMM_E_INVALID_ARG;
+  gemm_status st = check_problem(A, B, C, M, N, K);
+  if (st != GEMM_OK) return st;
+  st = check_current_device(p);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  const int64_t tm = ceil_div(M, p->desc.bm), tn = ceil_div(N, p->desc.bn);
+  const int64_t tiles = tm * tn;
+  if (tiles > GEMM_MAX_TILES) return GEMM_E_SHAPE;
+  KernelArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.single.A = static_cast<const uint16_t *>(A);
+  args.single.B = static_cast<const uint16_t *>(B);
+  args.single.C = C;
+  args.single.M = (int32_t)M;
+  args.single.N = (int32_t)N;
+  args.single.K = (int32_t)K;
+  args.single.tiles_m = (int32_t)tm;
+  args.single.tiles_n = (int32_t)tn;
+  args.single.tile_start = 0;
+  args.groups = nullptr;
+  args.G = 1;
+  p->last_tile_start.assign(1, 0);
+  return launch(p, sched_mode, false, args, tiles, static_cast<hipStream_t>(stream));
+}
+
+gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const *B, float *const *C,
+                             const int64_t *M, const int64_t *N, const int64_t *K, int32_t sched_mode,
+                             gemm_tile_cfg tile_cfg, void *stream) {
+  gemm_plan *p = tile_cfg;
+  if (!p) return GEMM_E_INVALID_ARG;
+  if (G <= 0 || !A || !B || !C || !M || !N || !K) return GEMM_E_INVALID_ARG;
+  if (G > p->desc.max_groups) return GEMM_E_SHAPE;
+  if (sched_mode < GEMM_SCHED_NONPERSISTENT || sched_mode > GEMM_SCHED_DYNAMIC) return GEMM_E_INVALID_ARG;
+  std::vector<KernelProblem> probs((size_t)G);
+  std::vector<int32_t> starts((size_t)G);
+  int64_t tiles = 0;
+  for (int32_t g = 0; g < G; ++g) {
+    gemm_status st = check_problem(A[g], B[g], C[g], M[g], N[g], K[g]);
+    if (st != GEMM_OK) return st;
+    KernelProblem &q = probs[(size_t)g];
+    q.A = static_cast<const uint16_t *>(A[g]);
+    q.B = static_cast<const uint16_t *>(B[g]);
+    q.C = C[g];
+    q.M = (int32_t)M[g];
+    q.N = (int32_t)N[g];
+    q.K = (int32_t)K[g];
+    q.tiles_m = (int32_t)ceil_div(M[g], p->desc.bm);
+    q.tiles_n = (int32_t)ceil_div(N[g], p->desc.bn);
+    q.tile_start = (int32_t)tiles;
+    starts[(size_t)g] = (int32_t)tiles;
+    tiles += (int64_t)q.tiles_m * q.tiles_n;
+    if (tiles > GEMM_MAX_TILES) return GEMM_E_SHAPE;
+  }
+  gemm_status st = check_current_device(p);
+  if (st != GEMM_OK) return st;
+  if (tiles == 0) return GEMM_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool same = p->last_groups.size() == probs.size() &&
+                    std::memcmp(p->last_groups.data(), probs.data(), sizeof(KernelProblem) * probs.size()) == 0;
+  if (!same) {
+    // the pinned staging may still be the source of an earlier upload
+    if (p->groups_event_pending) {
+      hipError_t e = hipEventSynchronize(p->groups_uploaded);
+      if (e != hipSuccess) return hip_fail(p, e, "hipEventSynchronize(groups)");
+    }
+    std::memcpy(p->h_groups, probs.data(), sizeof(KernelProblem) * probs.size());
+    hipError_t e = hipMemcpyAsync(p->d_groups, p->h_groups, sizeof(KernelProblem) * probs.size(),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(p, e, "hipMemcpyAsync(groups)");
+    e = hipEventRecord(p->groups_uploaded, s);
+    if (e != hipSuccess) return hip_fail(p, e, "hipEventRecord(groups)");
+    p->groups_event_pending = true;
+    p->last_groups = probs;
+  }
+  KernelArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.single = probs[0];
+  args.groups = p->d_groups;
+  args.G = G;
+  p->last_tile_start = starts;
+  return launch(p, sched_mode, true, args, tiles, s);
+}
+
+gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_t cap, size_t *n_out) {
+  gemm_plan *p = tile_cfg;
+  if (!p || !n_out || (cap > 0 && !host_out)) return GEMM_E_INVALID_ARG;
+  *n_out = 0;
+  if (!p->has_run || p->desc.log_capacity == 0) return GEMM_OK;
+  hipError_t e = hipStreamSynchronize(p->last_stream);
+  if (e != hipSuccess) return hip_fail(p, e, "hipStreamSynchronize");
+  const size_t n = (size_t)std::min<int64_t>(p->last_tiles, p->desc.log_capacity);
+  const size_t m = std::min(n, cap);
+  std::vector<TileRecDev> recs(m);
+  std::vector<uint32_t> visits(m);
+  SchedCtrl ctrl;
+  if (m > 0) {
+    e = hipMemcpy(recs.data(), p->d_log, sizeof(TileRecDev) * m, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(log)");
+    e = hipMemcpy(visits.data(), p->d_ctrl_block + sizeof(SchedCtrl), sizeof(uint32_t) * m, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(visits)");
+  }
+  e = hipMemcpy(&ctrl, p->d_ctrl_block, sizeof(ctrl), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(ctrl)");
+  for (size_t i = 0; i < m; ++i) {
+    gemm_tile_rec &r = host_out[i];
+    std::memset(&r, 0, sizeof(r));
+    r.visits = visits[i];
+    if (visits[i] == 0) {
+      r.tile = (uint32_t)i;
+      r.worker = 0xFFFFFFFFu;
+      continue;
+    }
+    r.tile = recs[i].tile;
+    r.worker = recs[i].worker;
+    r.hw_id = recs[i].hw_id;
+    r.xcc_id = recs[i].xcc_id;
+    r.t0 = recs[i].t0;
+    r.t1 = recs[i].t1;
+    r.r0 = recs[i].r0;
+    r.r1 = recs[i].r1;
+    const auto &ts = p->last_tile_start;
+    const auto it = std::upper_bound(ts.begin(), ts.end(), (int32_t)i);
+    r.problem = (uint32_t)(it - ts.begin() - 1);
+  }
+  *n_out = m;
+  if (ctrl.error != 0) {
+    p->last_error = "device-side scheduler error flags " + std::to_string(ctrl.error);
+    return (ctrl.error & 2u) ? GEMM_E_SCHED : GEMM_E_TIMEOUT;
+  }
+  return GEMM_OK;
+}
+
+gemm_status gemm_plan_info_get(gemm_tile_cfg tile_cfg, gemm_plan_info *out) {
+  gemm_plan *p = tile_cfg;
+  if (!p || !out) return GEMM_E_INVALID_ARG;
+  std::memset(out, 0, sizeof(*out));
+  out->device = p->desc.device;
+  out->cu_count = p->cu_count;
+  out->occupancy = p->occupancy;
+  out->static_workers = p->static_workers;
+  out->wallclock_khz = p->wallclock_khz;
+  out->last_tiles = p->last_tiles;
+  out->last_grid = p->last_grid;
+  out->last_mode = p->last_mode;
+  out->lds_bytes = p->lds_bytes;
+  return GEMM_OK;
+}
+
+gemm_status gemm_destroy(gemm_tile_cfg tile_cfg) {
+  gemm_plan *p = tile_cfg;
+  if (!p) return GEMM_OK;
+  if (p->has_run) (void)hipStreamSynchronize(p->last_stream);
+  if (p->groups_event_pending && p->groups_uploaded) (void)hipEventSynchronize(p->groups_uploaded);
+  if (p->d_ctrl_block) (void)hipFree(p->d_ctrl_block);
+  if (p->d_log) (void)hipFree(p->d_log);
+  if (p->d_groups) (void)hipFree(p->d_groups);
+  if (p->h_groups) (void)hipHostFree(p->h_groups);
+  if (p->groups_uploaded) (void)hipEventDestroy(p->groups_uploaded);
+  delete p;
+  return GEMM_OK;
+}
+
+const char *gemm_last_hip_error(gemm_tile_cfg tile_cfg) {
+  if (!tile_cfg) return "";
+  return tile_cfg->last_error.c_str();
+}
+
+gemm_status gemm_test_preset_counter(gemm_tile_cfg tile_cfg, uint32_t start) {
+  gemm_plan *p = tile_cfg;
+  if (!p) return GEMM_E_INVALID_ARG;
+  p->preset = start;
+  p->preset_pending = true;
+  return GEMM_OK;
+}
+
+gemm_status gemm_spoiler_run(int32_t device, int32_t n_wgs, int64_t spin_ns, void *stream, uint64_t *d_log,
+                             double wait_resident_ms) {
+  if (n_wgs <= 0 || spin_ns < 0 || spin_ns > 60ll * 1000 * 1000 * 1000) return GEMM_E_INVALID_ARG;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GEMM_E_HIP;
+  if (cur != device) return GEMM_E_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return GEMM_E_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_E_UNSUPPORTED;
+  if (n_wgs > prop.multiProcessorCount) return GEMM_E_INVALID_ARG;  // one workgroup per CU
+  int wclk = 0;
+  if (hipDeviceGetAttribute(&wclk, hipDeviceAttributeWallClockRate, device) != hipSuccess || wclk <= 0)
+    return GEMM_E_HIP;
+  // one host-visible residency counter per process (a device has its own launch order)
+  static uint32_t *resident = nullptr;
+  if (!resident) {
+    if (hipHostMalloc(&resident, 64, hipHostMallocCoherent) != hipSuccess) {
+      resident = nullptr;
+      return GEMM_E_NOMEM;
+    }
+  }
+  __atomic_store_n(resident, 0u, __ATOMIC_SEQ_CST);
+  const uint64_t ticks = (uint64_t)((double)spin_ns * (double)wclk / 1.0e6);
+  hipError_t e = ptg::launch_spoiler(n_wgs, ticks, resident, d_log, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return GEMM_E_HIP;
+  if (wait_resident_ms > 0) {
+    const auto t_end = std::chrono::steady_clock::now() + std::chrono::duration<double, std::milli>(wait_resident_ms);
+    while (__atomic_load_n(resident, __ATOMIC_SEQ_CST) < (uint32_t)n_wgs) {
+      if (std::chrono::steady_clock::now() > t_end) return GEMM_E_TIMEOUT;
+      std::this_thread::yield();
+    }
+  }
+  return GEMM_OK;
+}
+
+}  // extern "C"

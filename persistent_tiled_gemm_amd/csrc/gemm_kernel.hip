@@ -1,0 +1,398 @@
+// Persistent tiled bf16 GEMM for gfx950: C (fp32) = A (bf16, M x K) . B (bf16, K x N).
+//
+// One workgroup = 4 wave64s in a 2 x 2 arrangement; each wave owns a
+// (BM/2) x (BN/2) block of the output tile and accumulates it in fp32 with
+// v_mfma_f32_32x32x16_bf16. Operand tiles move global -> LDS with
+// buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR round trip) into two
+// LDS stages, so the loads of k-step kt+1 overlap the MFMAs of k-step kt.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so fragment reads are bank-conflict
+// free):
+//   A stage: BM rows x 64 k, 128 B per row; logical chunk c of row r sits in slot
+//            c ^ ((r ^ (r >> 3)) & 7). A fragments are read with ds_read_b128
+//            (8 consecutive k of one row per lane).
+//   B stage: 64 k rows x BN n; logical chunk c of row k sits in slot
+//            c ^ (10 (k & 1) + 4 ((k >> 1) & 1)). B fragments need 8 consecutive
+//            k of one column per lane; ds_read_b64_tr_b16 delivers them from the
+//            row-major (n-contiguous) tile: in each 16-lane group, lane L reads 4
+//            n values of row L/4 and lane i receives column i of the 4 x 16 block.
+// The MFMA is issued with the B fragment as its first operand, so the
+// accumulator of lane l holds four consecutive n of row m = l % 32, which the
+// epilogue writes as one 16-byte store.
+//
+// Scheduling: see the header comment of ptg_gemm.h. The work loop is the
+// persistent worker loop of the blog post "CUTLASS Cluster Launch Control
+// dynamic persistent kernel" (section "cancelling the launch, receiving the
+// work coordinate": compute the tile, fetch the next coordinate, stop on
+// failure); the claim-ahead and its LDS ring of response records follow its
+// section "following the CUTLASS source" (one elected producer thread, a
+// depth-3 response pipeline, a throttle on how far ahead claims run, consumers
+// check the success flag before the coordinate).
+#include "ptg_device.hpp"
+
+namespace ptg {
+
+template <int BM, int BN>
+struct Cfg {
+  static constexpr int BK = 64;
+  static constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
+  static constexpr int MI = WM / 32, NI = WN / 32;  // 32x32 MFMA blocks per wave
+  static constexpr int A_LOADS = BM / 32;           // 16-byte loads per thread per stage
+  static constexpr int B_LOADS = BN / 32;
+  static constexpr int A_STAGE = BM * BK * 2;       // bytes
+  static constexpr int B_STAGE = BK * BN * 2;
+  static constexpr int B_ROW = BN * 2;              // bytes per k row of the B stage
+  static constexpr int B_ROW_CHUNKS = BN / 8;
+  static constexpr int STAGE = A_STAGE + B_STAGE;
+  static constexpr int LDS = 2 * STAGE;
+};
+
+__device__ __forceinline__ uint32_t swz_a(uint32_t row) { return (row ^ (row >> 3)) & 7u; }
+__device__ __forceinline__ uint32_t swz_b(uint32_t k) { return 10u * (k & 1u) + 4u * ((k >> 1) & 1u); }
+
+// One record of the claim ring: the answer to one claim. `valid` is the success
+// predicate; `tile` is meaningful only when valid. `seq` is the worker's tile
+// ordinal the record answers (checked by the consumers).
+struct RingRec {
+  uint32_t tile, valid, seq, pad;
+};
+
+static constexpr int kRingDepth = 3;  // LDS slots; a run uses args.ring_depth (2 or 3) of them
+static constexpr uint32_t kGateSpinLimit = 1u << 22;  // x ~1.7 us sleeps: a few seconds at most
+
+__device__ __forceinline__ uint32_t claim_next(const KernelArgs &a) {
+  return __hip_atomic_fetch_add(&a.ctrl->counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + a.counter_base;
+}
+
+template <int BM, int BN, int MODE, bool GROUPED>
+__global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args) {
+  using CF = Cfg<BM, BN>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::LDS];
+  __shared__ RingRec ring[kRingDepth];
+  __shared__ uint32_t gate_ok;
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = wave_uniform(tid >> 6);
+  const uint32_t wm = wave >> 1, wn = wave & 1u;
+  const int32_t T = args.T;
+
+  // ---- optional concurrency gate: at most max_concurrent workgroups compute at once
+  if (args.max_concurrent > 0) {
+    if (tid == 0) {
+      uint32_t ok = 0;
+      for (uint32_t it = 0; it < kGateSpinLimit; ++it) {
+        uint32_t cur = __hip_atomic_load(&args.ctrl->gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (cur < (uint32_t)args.max_concurrent &&
+            __hip_atomic_compare_exchange_strong(&args.ctrl->gate, &cur, cur + 1u, __ATOMIC_ACQUIRE,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          ok = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(64);
+      }
+      if (!ok) __hip_atomic_fetch_or(&args.ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      gate_ok = ok;
+    }
+    __syncthreads();
+    if (!gate_ok) return;
+  }
+
+  // ---- first tile
+  uint32_t ord = 0;       // this worker's tile ordinal
+  uint32_t tile = 0;
+  bool valid = false;
+  uint32_t next_ord = 1;  // producer: next ordinal to claim
+  bool failed = false;    // producer: a claim has come back invalid
+  if constexpr (MODE == kDynamic) {
+    if (tid == 0) {
+      const uint32_t v = claim_next(args);
+      const uint32_t ok = v < (uint32_t)T ? 1u : 0u;
+      ring[0] = RingRec{v, ok, 0u, 0u};
+      failed = !ok;
+    }
+    __syncthreads();
+    tile = wave_uniform(ring[0].tile);
+    valid = wave_uniform(ring[0].valid) != 0;
+  } else {
+    tile = blockIdx.x;
+    valid = tile < (uint32_t)T;
+  }
+
+  uint32_t hwid = 0, xcc = 0;
+  if (tid == 0) {
+    hwid = read_hw_id();
+    xcc = read_xcc_id();
+  }
+
+  while (valid) {
+    // ---- decode the tile id
+    KernelProblem pb;
+    int32_t local = (int32_t)tile;
+    if constexpr (GROUPED) {
+      const int32_t g = find_problem(args.groups, args.G, (int32_t)tile);
+      pb = args.groups[g];
+      local -= pb.tile_start;
+    } else {
+      pb = args.single;
+    }
+    int32_t m_t, n_t;
+    decode_tile(local, pb.tiles_m, pb.tiles_n, args.raster_group, m_t, n_t);
+    const int32_t m0 = m_t * BM, n0 = n_t * BN;
+    const int32_t M = pb.M, N = pb.N, K = pb.K;
+
+    uint64_t t0 = 0, r0 = 0;
+    if (tid == 0) {
+      t0 = clock_core();
+      r0 = clock_wall();
+    }
+
+    // ---- claim ahead (the throttle: at most claims_ahead beyond the current tile)
+    uint32_t batch[2] = {0u, 0u};
+    uint32_t batch_ord = 0, batch_n = 0;
+    if constexpr (MODE == kDynamic) {
+      if (tid == 0 && !failed && args.claims_ahead >= 1) {
+        batch_ord = next_ord;
+        while (next_ord <= ord + (uint32_t)args.claims_ahead && batch_n < 2) {
+          batch[batch_n++] = claim_next(args);
+          ++next_ord;
+        }
+      }
+    }
+
+    // ---- per-thread load offsets for this tile (row / column edges masked)
+    uint32_t voff_a[CF::A_LOADS];
+    uint32_t kchunk_a[CF::A_LOADS];
+#pragma unroll
+    for (int j = 0; j < CF::A_LOADS; ++j) {
+      const uint32_t p = (uint32_t)(j * 4 + (int)wave) * 64u + lane;
+      const uint32_t row = p >> 3;
+      const uint32_t c = (p & 7u) ^ swz_a(row);
+      kchunk_a[j] = c * 8u;
+      voff_a[j] = (m0 + (int32_t)row < M) ? (row * (uint32_t)K + c * 8u) * 2u : kBufOob;
+    }
+    uint32_t voff_b[CF::B_LOADS];
+    uint32_t krow_b[CF::B_LOADS];
+#pragma unroll
+    for (int j = 0; j < CF::B_LOADS; ++j) {
+      const uint32_t p = (uint32_t)(j * 4 + (int)wave) * 64u + lane;
+      const uint32_t k = p / CF::B_ROW_CHUNKS;
+      const uint32_t c = (p % CF::B_ROW_CHUNKS) ^ swz_b(k);
+      krow_b[j] = k;
+      voff_b[j] = (n0 + (int32_t)(c * 8u) < N) ? (k * (uint32_t)N + c * 8u) * 2u : kBufOob;
+    }
+    const uint16_t *a_tile = pb.A + (size_t)m0 * (size_t)K;
+    const uint16_t *b_tile = pb.B + n0;
+    const int32_t nk = (K + CF::BK - 1) / CF::BK;
+    const int32_t full = K / CF::BK;  // k-steps with no K tail
+
+    auto issue_stage = [&](int st, int32_t kt) {
+      unsigned char *sa = smem + st * CF::STAGE;
+      unsigned char *sb = sa + CF::A_STAGE;
+      const int32_t k0 = kt * CF::BK;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + k0);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile + (size_t)k0 * (size_t)N);
+      const bool tail = kt >= full;
+#pragma unroll
+      for (int j = 0; j < CF::A_LOADS; ++j) {
+        uint32_t vo = voff_a[j];
+        if (tail && k0 + (int32_t)kchunk_a[j] >= K) vo = kBufOob;
+        load16_to_lds(ra, sa + (j * 4 + (int)wave) * 1024, vo);
+      }
+#pragma unroll
+      for (int j = 0; j < CF::B_LOADS; ++j) {
+        uint32_t vo = voff_b[j];
+        if (tail && k0 + (int32_t)krow_b[j] >= K) vo = kBufOob;
+        load16_to_lds(rb, sb + (j * 4 + (int)wave) * 1024, vo);
+      }
+    };
+
+    // fragment read offsets (bytes inside a stage)
+    uint32_t off_a[CF::MI];
+    uint32_t swa[CF::MI];
+#pragma unroll
+    for (int mi = 0; mi < CF::MI; ++mi) {
+      const uint32_t row = wm * CF::WM + mi * 32 + (lane & 31u);
+      off_a[mi] = row * 128u;
+      swa[mi] = swz_a(row) ^ (lane >> 5);
+    }
+    uint32_t off_b[CF::NI];
+    {
+      const uint32_t q = lane >> 4, i = lane & 15u, h = q >> 1;
+      const uint32_t kk = 8u * h + (i >> 2);
+#pragma unroll
+      for (int ni = 0; ni < CF::NI; ++ni) {
+        const uint32_t n = wn * CF::WN + ni * 32 + 16u * (q & 1u) + 4u * (i & 3u);
+        off_b[ni] = kk * CF::B_ROW + (((n >> 3) ^ swz_b(kk)) << 4) + ((n & 7u) << 1);
+      }
+    }
+
+    f32x16 acc[CF::MI][CF::NI];
+#pragma unroll
+    for (int mi = 0; mi < CF::MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < CF::NI; ++ni)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
+
+    if (nk > 0) {
+      issue_stage(0, 0);
+      wait_vmem_all();
+      wg_barrier();
+      for (int32_t kt = 0; kt < nk; ++kt) {
+        const int st = kt & 1;
+        if (kt + 1 < nk) issue_stage(st ^ 1, kt + 1);
+        const unsigned char *sa = smem + st * CF::STAGE;
+        const unsigned char *sb = sa + CF::A_STAGE;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8 af[CF::MI];
+          bf16x8 bfr[CF::NI];
+#pragma unroll
+          for (int mi = 0; mi < CF::MI; ++mi)
+            af[mi] = *(const bf16x8 *)(sa + off_a[mi] + ((((uint32_t)(2 * s)) ^ swa[mi]) << 4));
+#pragma unroll
+          for (int ni = 0; ni < CF::NI; ++ni) {
+            const unsigned char *pb0 = sb + off_b[ni] + (16 * s) * CF::B_ROW;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0 + 4 * CF::B_ROW));
+            typedef __attribute__((ext_vector_type(8))) short i16x8;
+            const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            bfr[ni] = __builtin_bit_cast(bf16x8, v);
+          }
+#pragma unroll
+          for (int mi = 0; mi < CF::MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < CF::NI; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+        }
+        wait_vmem_all();
+        wg_barrier();
+      }
+    }
+
+    // ---- epilogue: fp32 accumulators -> C (lane holds 4 consecutive n of one m)
+#pragma unroll
+    for (int mi = 0; mi < CF::MI; ++mi) {
+      const int32_t m = m0 + (int32_t)(wm * CF::WM + mi * 32 + (lane & 31u));
+#pragma unroll
+      for (int ni = 0; ni < CF::NI; ++ni) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int32_t n = n0 + (int32_t)(wn * CF::WN + ni * 32 + 8 * qd + 4 * (lane >> 5));
+          if (m < M && n < N) {
+            f32x4 v = {acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1], acc[mi][ni][4 * qd + 2],
+                       acc[mi][ni][4 * qd + 3]};
+            *(f32x4 *)(pb.C + (size_t)m * (size_t)N + n) = v;
+          }
+        }
+      }
+    }
+
+    // ---- publish the next claim (producer) and log the tile
+    if (tid == 0) {
+      if constexpr (MODE == kDynamic) {
+        if (args.claims_ahead == 0 && !failed) {
+          batch_ord = next_ord;
+          batch[0] = claim_next(args);
+          batch_n = 1;
+          ++next_ord;
+        }
+        for (uint32_t b = 0; b < batch_n; ++b) {
+          const uint32_t v = batch[b];
+          const uint32_t ok = v < (uint32_t)T ? 1u : 0u;
+          if (!ok) failed = true;
+          ring[(batch_ord + b) % (uint32_t)args.ring_depth] = RingRec{v, ok, batch_ord + b, 0u};
+        }
+      }
+      const uint64_t t1 = clock_core();
+      const uint64_t r1 = clock_wall();
+      if ((int32_t)tile < args.log_cap) {
+        TileRecDev rec;
+        rec.tile = tile;
+        rec.worker = blockIdx.x;
+        rec.hw_id = hwid;
+        rec.xcc_id = xcc;
+        rec.t0 = t0;
+        rec.t1 = t1;
+        rec.r0 = r0;
+        rec.r1 = r1;
+        args.log[tile] = rec;
+        __hip_atomic_fetch_add(&args.visits[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+
+    // ---- advance
+    if constexpr (MODE == kDynamic) {
+      __syncthreads();
+      const RingRec rec = ring[(ord + 1) % (uint32_t)args.ring_depth];
+      const uint32_t seq = wave_uniform(rec.seq);
+      valid = wave_uniform(rec.valid) != 0;
+      tile = wave_uniform(rec.tile);
+      if (seq != ord + 1) {
+        // the ring protocol was violated: stop this worker and flag it
+        if (tid == 0) __hip_atomic_fetch_or(&args.ctrl->error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        valid = false;
+      }
+    } else if constexpr (MODE == kStatic) {
+      tile += (uint32_t)args.P;
+      valid = tile < (uint32_t)T;
+    } else {
+      valid = false;
+    }
+    ++ord;
+  }
+
+  if (args.max_concurrent > 0 && tid == 0) {
+    __hip_atomic_fetch_sub(&args.ctrl->gate, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int BM, int BN, int MODE, bool GROUPED>
+static hipError_t launch_one(const KernelArgs &args, int grid, int dyn_lds, hipStream_t stream) {
+  hipLaunchKernelGGL((ptg_gemm_kernel<BM, BN, MODE, GROUPED>), dim3(grid), dim3(256), dyn_lds, stream, args);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+static hipError_t launch_tile(int mode, bool grouped, const KernelArgs &args, int grid, int dyn_lds,
+                              hipStream_t stream) {
+  switch (mode) {
+    case kNonPersistent:
+      return grouped ? launch_one<BM, BN, kNonPersistent, true>(args, grid, dyn_lds, stream)
+                     : launch_one<BM, BN, kNonPersistent, false>(args, grid, dyn_lds, stream);
+    case kStatic:
+      return grouped ? launch_one<BM, BN, kStatic, true>(args, grid, dyn_lds, stream)
+                     : launch_one<BM, BN, kStatic, false>(args, grid, dyn_lds, stream);
+    case kDynamic:
+      return grouped ? launch_one<BM, BN, kDynamic, true>(args, grid, dyn_lds, stream)
+                     : launch_one<BM, BN, kDynamic, false>(args, grid, dyn_lds, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm(int tile_edge, int mode, bool grouped, const KernelArgs &args, int grid, int dyn_lds,
+                       hipStream_t stream) {
+  if (tile_edge == 256) return launch_tile<256, 256>(mode, grouped, args, grid, dyn_lds, stream);
+  if (tile_edge == 128) return launch_tile<128, 128>(mode, grouped, args, grid, dyn_lds, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t gemm_occupancy(int tile_edge, int dyn_lds, int *blocks_per_cu) {
+  if (tile_edge == 256)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<256, 256, kDynamic, false>), 256, dyn_lds);
+  if (tile_edge == 128)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<128, 128, kDynamic, false>), 256, dyn_lds);
+  return hipErrorInvalidValue;
+}
+
+int gemm_static_lds_bytes(int tile_edge) {
+  if (tile_edge == 256) return Cfg<256, 256>::LDS + (int)sizeof(RingRec) * kRingDepth + 4;
+  if (tile_edge == 128) return Cfg<128, 128>::LDS + (int)sizeof(RingRec) * kRingDepth + 4;
+  return 0;
+}
+
+}  // namespace ptg

@@ -1,0 +1,93 @@
+// Device-side building blocks of the persistent tiled GEMM (gfx950 only):
+// operand types, buffer resources with out-of-range masking, timers and
+// hardware ids, the tile raster and the claim-ring record.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ptg_internal.hpp"
+
+namespace ptg {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Buffer resource over a base pointer. Offsets at or above kBufRecords read as
+// zero (hardware range check), which is how edge rows/columns and the K tail
+// are masked: a lane whose chunk lies outside the matrix gets kBufOob.
+static constexpr uint32_t kBufRecords = 0x40000000u;
+static constexpr uint32_t kBufOob = 0x40000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
+  // word 3 = 0x00020000: raw (untyped) 32-bit data format for gfx9-family buffers
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)kBufRecords, 0x00020000);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + lane*16
+// (lds_base is wave-uniform; it goes to M0).
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void *lds_base, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)lds_base, 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Execution barrier for the workgroup without the full-memory fence of
+// __syncthreads (the direct-to-LDS loads are waited for explicitly).
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint64_t clock_core() { return __builtin_amdgcn_s_memtime(); }
+__device__ __forceinline__ uint64_t clock_wall() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ uint32_t read_hw_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t read_xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Tile id -> (m_t, n_t) inside one problem. Row-major, or grouped-M: groups of
+// `group` tile rows, column-major inside a group (so consecutive ids share B
+// column panels and a few A row panels).
+__device__ __forceinline__ void decode_tile(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t group,
+                                            int32_t &m_t, int32_t &n_t) {
+  if (group <= 1) {
+    m_t = t / tiles_n;
+    n_t = t - m_t * tiles_n;
+    return;
+  }
+  const int32_t per_group = group * tiles_n;
+  const int32_t g = t / per_group;
+  const int32_t first_m = g * group;
+  int32_t gm = tiles_m - first_m;
+  gm = gm < group ? gm : group;
+  const int32_t r = t - g * per_group;
+  m_t = first_m + r % gm;
+  n_t = r / gm;
+}
+
+// Which problem of a grouped launch owns global tile id t (tile_start ascending).
+__device__ __forceinline__ int32_t find_problem(const KernelProblem *probs, int32_t G, int32_t t) {
+  int32_t lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (probs[mid].tile_start <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace ptg

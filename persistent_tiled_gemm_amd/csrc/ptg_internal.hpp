@@ -1,0 +1,64 @@
+// Types shared by the host library and the kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ptg {
+
+// One GEMM problem as the kernel sees it. Grouped launches pass an array of
+// these in device memory; a single GEMM passes one by value.
+struct KernelProblem {
+  const uint16_t *A;   // M x K bf16 bits, row-major
+  const uint16_t *B;   // K x N bf16 bits, row-major
+  float *C;            // M x N fp32, row-major
+  int32_t M, N, K;
+  int32_t tiles_m, tiles_n;
+  int32_t tile_start;  // first global tile id of this problem
+};
+
+// Scheduler state in device memory, cleared before every run that uses it.
+struct alignas(64) SchedCtrl {
+  uint32_t counter;    // dynamic claim counter
+  uint32_t gate;       // workgroups currently holding a concurrency slot
+  uint32_t error;      // bit 0: a gate wait ran out
+  uint32_t pad[13];
+};
+
+// Tile-log record as written by the kernel (tile-indexed).
+struct TileRecDev {
+  uint32_t tile, worker, hw_id, xcc_id;
+  uint64_t t0, t1, r0, r1;
+};
+static_assert(sizeof(TileRecDev) == 48, "tile record layout");
+
+struct KernelArgs {
+  KernelProblem single;         // the problem when G == 1 and !grouped
+  const KernelProblem *groups;  // device array (grouped launches)
+  int32_t G;
+  int32_t T;                    // total tiles
+  int32_t P;                    // static stride (grid size of a static run)
+  int32_t claims_ahead;         // 0, 1 or 2 (< ring_depth)
+  int32_t ring_depth;           // 2 or 3
+  int32_t raster_group;         // <= 1: row-major
+  uint32_t counter_base;        // added to every claim (failure forcing)
+  int32_t max_concurrent;       // 0: no gate
+  int32_t log_cap;              // tiles logged (0: none)
+  SchedCtrl *ctrl;
+  TileRecDev *log;
+  uint32_t *visits;
+};
+
+enum SchedMode { kNonPersistent = 0, kStatic = 1, kDynamic = 2 };
+
+// Launch one GEMM kernel instance. tile_edge is 128 or 256.
+hipError_t launch_gemm(int tile_edge, int mode, bool grouped, const KernelArgs &args, int grid,
+                       int dyn_lds_bytes, hipStream_t stream);
+// Resident workgroups per CU for an instance with dyn_lds_bytes of extra LDS.
+hipError_t gemm_occupancy(int tile_edge, int dyn_lds_bytes, int *blocks_per_cu);
+// Static LDS of an instance, bytes.
+int gemm_static_lds_bytes(int tile_edge);
+
+hipError_t launch_spoiler(int n_wgs, uint64_t spin_ticks, uint32_t *resident, uint64_t *log, hipStream_t stream);
+
+}  // namespace ptg

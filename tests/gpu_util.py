@@ -1,0 +1,76 @@
+"""Helpers shared by the GPU tests: upload seeded inputs, run through the C ABI,
+compare with the oracle, check the tile log."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import persistent_tiled_gemm_amd as ptg
+from oracle.gemm_ref import check_result, decode_bf16, gemm_ref, gemm_ref_rows
+from oracle.ownership import check_ownership
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def upload(problem):
+    A = ptg.bf16_from_bits(problem.a_bits)
+    B = ptg.bf16_from_bits(problem.b_bits)
+    return A, B
+
+
+def new_c(M, N, fill=float("nan")):
+    torch = torch_mod()
+    return torch.full((M, N), fill, dtype=torch.float32, device="cuda")
+
+
+def make_plan(tile=256, **kw):
+    kw.setdefault("log_capacity", 1 << 14)
+    return ptg.gemm_create(tile_edge=tile, **kw)
+
+
+def run(problem, plan, mode, C=None, stream=None):
+    A, B = upload(problem)
+    if C is None:
+        C = new_c(problem.M, problem.N)
+    ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
+    torch_mod().cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def maxabs(bits):
+    return float(np.abs(decode_bf16(bits)).max()) if bits.size else 0.0
+
+
+def assert_close_full(problem, c_gpu):
+    ref = gemm_ref(problem.a_bits, problem.b_bits)
+    rep = check_result(c_gpu, ref, problem.K, maxabs(problem.a_bits), maxabs(problem.b_bits))
+    assert rep["ok"], rep
+    return rep
+
+
+def assert_close_rows(problem, c_gpu, rows):
+    rows = np.asarray(sorted(set(int(r) for r in rows)))
+    ref = gemm_ref_rows(problem.a_bits, problem.b_bits, rows)
+    rep = check_result(c_gpu[rows], ref, problem.K, maxabs(problem.a_bits), maxabs(problem.b_bits))
+    assert rep["ok"], rep
+    return rep
+
+
+def check_log(plan, mode, T, P=None, expected_tiles=None):
+    log = ptg.gemm_read_log(plan)
+    assert len(log) == T, (len(log), T)
+    ran = log[log["visits"] > 0]
+    errs = check_ownership(mode, T, ran["tile"], ran["worker"], ran["r0"].astype(np.float64),
+                           ran["r1"].astype(np.float64), log["visits"], P=P, expected_tiles=expected_tiles)
+    assert not errs, errs
+    return log

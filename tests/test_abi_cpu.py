@@ -1,0 +1,69 @@
+"""The C-ABI library loads and exports every function include/ptg_gemm.h declares (CPU only).
+
+No compute call is made here; only argument checks that return before any HIP
+call (null handles, bad enums, descriptor defaults) are exercised.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import persistent_tiled_gemm_amd as ptg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ptg_gemm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(gemm_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ptg.LIB_PATH):
+        pytest.fail(f"{ptg.LIB_PATH} not built (run python -m persistent_tiled_gemm_amd.build)")
+    return ptg.load_library()
+
+
+def test_header_declares_the_abi():
+    names = _declared_functions()
+    assert set(names) == set(ptg.ABI_FUNCTIONS), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", ptg.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(gemm_[a-z_0-9]+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_defaults(lib):
+    assert ptg.gemm_status_str(0) == "ok"
+    for s in range(-8, 0):
+        assert ptg.gemm_status_str(s) not in ("", "unknown status")
+    assert ptg.gemm_status_str(-99) == "unknown status"
+    d = ptg.gemm_default_desc(256, 0)
+    assert (d.bm, d.bn, d.bk, d.ring_depth, d.claims_ahead) == (256, 256, 64, 3, 1)
+    d = ptg.gemm_default_desc(128, 0)
+    assert (d.bm, d.bn) == (128, 128)
+    with pytest.raises(ptg.PtgError):
+        ptg.gemm_default_desc(192, 0)
+
+
+def test_null_arguments_are_rejected_before_any_hip_call(lib):
+    assert lib.gemm_create(None, None) == -1
+    assert lib.gemm_run(None, None, None, 8, 8, 8, 2, None, None) == -1
+    assert lib.gemm_run_grouped(1, None, None, None, None, None, None, 2, None, None) == -1
+    n = ctypes.c_size_t(0)
+    assert lib.gemm_read_log(None, None, 0, ctypes.byref(n)) == -1
+    assert lib.gemm_plan_info_get(None, None) == -1
+    assert lib.gemm_destroy(None) == 0
+    assert lib.gemm_test_preset_counter(None, 3) == -1
+    assert lib.gemm_last_hip_error(None) == b""
+    assert lib.gemm_spoiler_run(0, 0, 1000, None, None, 0.0) == -1

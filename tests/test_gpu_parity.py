@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Tolerance (the stated acceptance for bf16 inputs with fp32 accumulation):
+relative Frobenius error <= 1e-3 and per element
+|err| <= 1e-2 * sqrt(K) * max|a| * max|b| * 2^-8. Integer-valued inputs whose
+partial sums stay below 2^24 are exact in fp32 and must match bit for bit;
+identity and permutation operands must reproduce the other operand exactly.
+The tile log must be exactly-once for every run (bit-exact ownership checks).
+"""
+
+import numpy as np
+import pytest
+
+import persistent_tiled_gemm_amd as ptg
+from tests.gpu_util import (assert_close_full, check_log, make_plan, new_c, run, say, torch_mod, upload)
+from workloads import f32_to_bf16_bits, make_problem
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("nonpersistent", "static", "dynamic")
+
+# shapes spanning several tiles with ragged tails in M, N and K
+SMALL_SHAPES = [
+    (384, 512, 512),    # the twelve 128x128 tiles of the worked example
+    (256, 256, 64),     # one 256 tile, one k-step
+    (1000, 776, 264),   # ragged M, N, K
+    (513, 264, 72),
+    (1, 8, 8),          # degenerate: one row, one k chunk
+    (700, 1032, 1240),
+]
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+def test_small_shapes_all_modes(tile, shape):
+    M, N, K = shape
+    p = make_problem(M, N, K, "uniform", seed=M + N + K)
+    plan = make_plan(tile)
+    outs = {}
+    for mode in MODES:
+        say(f"case tile={tile} shape={shape} mode={mode}")
+        c = run(p, plan, mode)
+        assert_close_full(p, c)
+        T = -(-M // tile) * -(-N // tile)
+        info = ptg.gemm_plan_info_get(plan)
+        check_log(plan, mode, T, P=info["last_grid"] if mode == "static" else None)
+        outs[mode] = c
+    # scheduling never changes numerics: same tile code, same k order
+    assert np.array_equal(outs["static"], outs["dynamic"])
+    assert np.array_equal(outs["nonpersistent"], outs["dynamic"])
+    plan.destroy()
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+def test_integer_inputs_bit_exact(tile):
+    rng = np.random.default_rng(5)
+    M, N, K = 520, 776, 1032  # |partial sums| <= 64 K < 2^24
+    ai = rng.integers(-8, 9, size=(M, K))
+    bi = rng.integers(-8, 9, size=(K, N))
+    from workloads import GemmProblem
+    p = GemmProblem(f32_to_bf16_bits(ai.astype(np.float32)), f32_to_bf16_bits(bi.astype(np.float32)))
+    exact = (ai @ bi).astype(np.float32)
+    plan = make_plan(tile)
+    for mode in MODES:
+        say(f"case integer tile={tile} mode={mode}")
+        c = run(p, plan, mode)
+        assert np.array_equal(c, exact)
+    plan.destroy()
+
+
+def test_identity_and_permutation_reproduce_operands():
+    K = 512
+    p = make_problem(K, 264, K, "normal", seed=9)
+    eye = f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    perm = np.random.default_rng(2).permutation(K)
+    pm = f32_to_bf16_bits(np.eye(K, dtype=np.float32)[perm])
+    from workloads import GemmProblem
+    b_vals = ((p.b_bits.astype(np.uint32) << 16).view(np.float32))
+    plan = make_plan(256)
+    for mode in MODES:
+        say(f"case identity mode={mode}")
+        c = run(GemmProblem(eye, p.b_bits), plan, mode)
+        assert np.array_equal(c, b_vals)
+        c = run(GemmProblem(pm, p.b_bits), plan, mode)
+        assert np.array_equal(c, b_vals[perm])
+        # identity on the right reproduces A (rows of 264 are not a tile multiple)
+        q = make_problem(300, K, K, "uniform", seed=4)
+        c = run(GemmProblem(q.a_bits, eye), plan, mode)
+        assert np.array_equal(c, (q.a_bits.astype(np.uint32) << 16).view(np.float32))
+    plan.destroy()
+
+
+def test_empty_and_degenerate_inputs():
+    torch = torch_mod()
+    plan = make_plan(256)
+    A = torch.zeros((16, 8), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")
+    # M == 0 / N == 0: nothing enqueued, C untouched
+    C = new_c(0, 16)
+    ptg.gemm_run(torch.zeros((0, 8), dtype=torch.bfloat16, device="cuda"), B, C, plan)
+    C2 = new_c(16, 0)
+    ptg.gemm_run(A, torch.zeros((8, 0), dtype=torch.bfloat16, device="cuda"), C2, plan)
+    # K == 0: C is all zeros
+    for mode in MODES:
+        C3 = new_c(300, 264)
+        ptg.gemm_run(torch.zeros((300, 0), dtype=torch.bfloat16, device="cuda"),
+                     torch.zeros((0, 264), dtype=torch.bfloat16, device="cuda"), C3, plan, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(C3).item() == 0 and not torch.isnan(C3).any().item()
+    # shape errors come back as status codes, nothing is enqueued
+    C4 = new_c(16, 12)
+    st = ptg.gemm_run_raw(A.data_ptr(), torch.zeros((8, 12), dtype=torch.bfloat16, device="cuda").data_ptr(),
+                          C4.data_ptr(), 16, 12, 8, plan)
+    assert st == -2  # N not a multiple of 8
+    assert ptg.gemm_run_raw(A.data_ptr(), B.data_ptr(), C4.data_ptr(), 16, 16, 12, plan) == -2  # K % 8
+    assert ptg.gemm_run_raw(0, B.data_ptr(), C4.data_ptr(), 16, 16, 8, plan) == -1
+    assert ptg.gemm_run_raw(A.data_ptr(), B.data_ptr(), C4.data_ptr(), 16, 16, 8, plan, mode=7) == -1
+    assert ptg.gemm_run_raw(A.data_ptr() + 2, B.data_ptr(), C4.data_ptr(), 16, 16, 8, plan) == -1  # misaligned
+    assert ptg.gemm_run_raw(A.data_ptr(), B.data_ptr(), C4.data_ptr(), -1, 16, 8, plan) == -2
+    assert ptg.gemm_run_raw(A.data_ptr(), B.data_ptr(), C4.data_ptr(), 16, 16, (1 << 20) + 8, plan) == -2
+    torch.cuda.synchronize()
+    assert torch.isnan(C4).all().item()
+    plan.destroy()
+
+
+def test_plan_validation():
+    for bad in ({"tile_edge": 256, "claims_ahead": 3}, {"tile_edge": 256, "ring_depth": 4},
+                {"tile_edge": 256, "ring_depth": 2, "claims_ahead": 2}, {"tile_edge": 256, "raster": 2},
+                {"tile_edge": 256, "device": 99}):
+        with pytest.raises(ptg.PtgError):
+            ptg.gemm_create(**bad)
+    d = ptg.gemm_default_desc(256, 0)
+    d.bk = 32
+    with pytest.raises(ptg.PtgError) as e:
+        ptg.Plan(d)
+    assert e.value.status == -3
+    plan = ptg.gemm_create(tile_edge=256)
+    info = ptg.gemm_plan_info_get(plan)
+    assert info["cu_count"] > 0 and info["occupancy"] >= 1 and info["wallclock_khz"] > 0
+    assert info["static_workers"] == info["occupancy"] * info["cu_count"]
+    plan.destroy()
+
+
+@pytest.mark.parametrize("q,depth", [(0, 3), (1, 3), (2, 3), (1, 2), (0, 2)])
+def test_claims_ahead_variants(q, depth):
+    p = make_problem(1280, 1024, 512, "uniform", seed=q * 10 + depth)
+    plan = make_plan(256, claims_ahead=q, ring_depth=depth)
+    say(f"case claims_ahead={q} depth={depth}")
+    c = run(p, plan, "dynamic")
+    assert_close_full(p, c)
+    check_log(plan, "dynamic", 20)
+    plan.destroy()
+
+
+@pytest.mark.parametrize("group", [1, 3, 8])
+def test_grouped_raster(group):
+    p = make_problem(1800, 1288, 200, "uniform", seed=group)
+    plan = make_plan(256, raster=1, raster_group=group)
+    for mode in MODES:
+        say(f"case raster group={group} mode={mode}")
+        c = run(p, plan, mode)
+        assert_close_full(p, c)
+        T = 8 * 6
+        info = ptg.gemm_plan_info_get(plan)
+        check_log(plan, mode, T, P=info["last_grid"] if mode == "static" else None)
+    plan.destroy()
+
+
+def test_static_with_few_workers():
+    # P smaller than the tile count: each worker walks w, w+P, ... (the tile sequence of the worked example)
+    p = make_problem(1024, 1024, 256, "uniform", seed=3)
+    plan = make_plan(256, static_workers=5)
+    c = run(p, plan, "static")
+    assert_close_full(p, c)
+    log = check_log(plan, "static", 16, P=5)
+    for w in range(5):
+        assert sorted(log["tile"][log["worker"] == w].tolist()) == list(range(w, 16, 5))
+    plan.destroy()
+
+
+def test_logging_off_still_computes():
+    p = make_problem(600, 520, 328, "uniform", seed=12)
+    plan = ptg.gemm_create(tile_edge=128, log_capacity=0)
+    for mode in MODES:
+        c = run(p, plan, mode)
+        assert_close_full(p, c)
+    assert len(ptg.gemm_read_log(plan)) == 0
+    plan.destroy()
+
+
+def test_failure_forcing_counter_preset():
+    # the counter starts at s: exactly tiles s..T-1 run, every worker's claims fail after that,
+    # late slots exit at once, and the C rows of tiles < s are never written (stay NaN)
+    torch = torch_mod()
+    p = make_problem(2048, 512, 256, "uniform", seed=8)  # 8 x 2 tiles of 256
+    T = 16
+    plan = make_plan(256)
+    for s in (0, 5, 15, 16, 40):
+        say(f"case preset counter start={s}")
+        A, B = upload(p)
+        C = new_c(p.M, p.N)
+        ptg.gemm_test_preset_counter(plan, s)
+        ptg.gemm_run(A, B, C, plan, mode="dynamic")
+        torch.cuda.synchronize()
+        c = C.cpu().numpy()
+        expected = list(range(s, T))
+        check_log(plan, "dynamic", T, expected_tiles=expected)
+        for k in range(T):
+            mt, nt = divmod(k, 2)
+            blk = c[mt * 256:(mt + 1) * 256, nt * 256:(nt + 1) * 256]
+            if k >= s:
+                assert not np.isnan(blk).any()
+            else:
+                assert np.isnan(blk).all()
+    # the preset applies to one run only
+    c = run(p, plan, "dynamic")
+    assert_close_full(p, c)
+    check_log(plan, "dynamic", T)
+    plan.destroy()
