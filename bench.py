@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark: bf16 GEMM TFLOP/s and % of MFMA peak on 8192^3; tail makespans.
+
+One step = one pass of the whole hot path: a gemm_run of the dynamic scheduler
+(atomic claim counter + LDS claim ring) on M = N = K = 8192, 256x256x64 tiles,
+A and B i.i.d. N(0,1)/sqrt(K) in bf16, fp32 C, tile log on. Inputs are resident
+in HBM before timing starts. The kernel time is measured with HIP events on
+the stream the kernel is launched on.
+
+Printed: ONE JSON line with the contract fields, a `roofline` object for the
+GEMM kernel, a `cpu_baseline` object (the CPU oracle timed on a bounded row
+sample of the same workload), the static / non-persistent modes at the same
+shape, and (unless --no-tail) the tail makespans of the partial-occupancy,
+uneven-cost grouped, tail-boundary and worked-example workloads.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "bf16 GEMM TFLOP/s and % MFMA peak; tail makespan static vs dynamic"
+KERNEL_SOURCES = ("persistent_tiled_gemm_amd/csrc/gemm_kernel.hip", "persistent_tiled_gemm_amd/csrc/ptg_device.hpp",
+                  "persistent_tiled_gemm_amd/csrc/ptg_internal.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_square_8192_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_units: float):
+    """HBM bytes per launch from the committed counter runs, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_runs(fn, steps: int, warmup: int, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+def cu_key(hw_id, xcc_id):
+    """Physical CU identity from the HW_ID register (cu, sh, se fields, bits 8..15) and the XCC id."""
+    return (xcc_id.astype(np.int64) << 8) | ((hw_id.astype(np.int64) >> 8) & 0xFF)
+
+
+def makespan_from_log(rec, khz):
+    ran = rec[rec["visits"] > 0]
+    if len(ran) == 0:
+        return None
+    r0 = ran["r0"].astype(np.float64)
+    r1 = ran["r1"].astype(np.float64)
+    span_us = (r1.max() - r0.min()) / khz * 1e3
+    dur_us = (r1 - r0) / khz * 1e3
+    return {"makespan_us": span_us, "tile_median_us": float(np.median(dur_us)), "tiles": int(len(ran)),
+            "workers": int(len(np.unique(ran["worker"]))), "cus": int(len(np.unique(cu_key(ran["hw_id"], ran["xcc_id"]))))}
+
+
+def cpu_baseline(problem, target_s: float = 10.0):
+    """Time the CPU oracle (gemm_ref_rows: exact bf16 decode + fp64 product) on a row sample."""
+    from oracle.gemm_ref import gemm_ref_rows
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    M, K = problem.a_bits.shape
+    N = problem.b_bits.shape[1]
+    rows = 256
+    t0 = time.perf_counter()
+    gemm_ref_rows(problem.a_bits, problem.b_bits, range(rows))
+    t = time.perf_counter() - t0
+    rows = int(min(M, max(256, rows * target_s / max(t, 1e-3))))
+    t0 = time.perf_counter()
+    gemm_ref_rows(problem.a_bits, problem.b_bits, range(rows))
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} of {M} rows of C (all {N} columns, K={K}), fp64, {t:.2f} s"}
+
+
+def run_tail_sections(ptg, torch, stream, khz, square):
+    """Makespans per scheduler on the partial-occupancy, grouped, tail-boundary and worked-example workloads."""
+    from oracle.sched_model import simulate
+    from workloads import make_problem, make_workload
+    out = {}
+    modes = ("nonpersistent", "static", "dynamic")
+
+    # partial occupancy: 8192^3 co-run with a 64-CU spoiler spinning 2 ms
+    log("tail: partial occupancy")
+    p, A, B, C = square
+    plan = ptg.gemm_create(tile_edge=256, log_capacity=1024)
+    spoil_stream = torch.cuda.Stream()
+    res = {}
+    for mode in modes:
+        ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)  # warm
+        torch.cuda.synchronize()
+        spoiler_log = torch.zeros(64 * 4, dtype=torch.int64, device="cuda")
+        ptg.gemm_spoiler_run(64, 2_000_000, stream=spoil_stream, log=spoiler_log, wait_resident_ms=2000.0)
+        ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
+        torch.cuda.synchronize()
+        rec = ptg.gemm_read_log(plan)
+        ms = makespan_from_log(rec, khz)
+        sl = spoiler_log.cpu().numpy().reshape(64, 4).astype(np.float64)
+        ms["spoiler_cus"] = int(len(np.unique(cu_key(sl[:, 2].astype(np.int64), sl[:, 3].astype(np.int64)))))
+        ran = rec[rec["visits"] > 0]
+        ms["spoiler_end_after_first_tile_us"] = float((sl[:, 1].max() - ran["r0"].min()) / khz * 1e3)
+        res[mode] = ms
+    t_free = res["static"]["tile_median_us"]
+    for mode in modes:
+        res[mode]["makespan_t"] = res[mode]["makespan_us"] / t_free
+    tau = max(res["static"]["spoiler_end_after_first_tile_us"], 0.0) / t_free
+    avail = [0.0] * 192 + [tau] * 64
+    res["model_t"] = {m: simulate([1.0] * 1024, m, avail=avail, P=256).makespan for m in modes}
+    res["dynamic_beats_static"] = bool(res["dynamic"]["makespan_us"] < res["static"]["makespan_us"])
+    out["partial_occupancy"] = res
+    plan.destroy()
+
+    # uneven-cost grouped: 64 x (1024 x 1024, K_g = 512 U{1..16})
+    log("tail: grouped uneven")
+    w = make_workload("grouped_uneven")
+    As = [ptg.bf16_from_bits(q.a_bits) for q in w.problems]
+    Bs = [ptg.bf16_from_bits(q.b_bits) for q in w.problems]
+    Cs = [torch.empty((q.M, q.N), dtype=torch.float32, device="cuda") for q in w.problems]
+    plan = ptg.gemm_create(tile_edge=256, log_capacity=1024)
+    res = {}
+    ks = np.array([q.K for q in w.problems])
+    for mode in modes:
+        ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode, stream=stream)
+        torch.cuda.synchronize()
+        ms_ev = time_runs(lambda: ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode, stream=stream), 5, 1, stream)
+        ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode, stream=stream)
+        rec = ptg.gemm_read_log(plan)
+        ms = makespan_from_log(rec, khz)
+        ms["kernel_ms"] = ms_ev
+        ms["tflops"] = w.flops / (ms_ev * 1e-3) / 1e12
+        res[mode] = ms
+        if mode == "static":
+            ran = rec[rec["visits"] > 0]
+            dur = ((ran["r1"] - ran["r0"]).astype(np.float64) / khz * 1e3)
+            kt = ks[ran["problem"]] / 64.0
+            alpha, beta = np.polyfit(kt, dur, 1)
+    costs = [alpha * (ks[t // 16] / 64.0) + beta for t in range(1024)]
+    res["model_us"] = {m: simulate(costs, m, slots=256, P=256).makespan for m in modes}
+    res["cost_fit_us"] = {"per_kstep": float(alpha), "fixed": float(beta)}
+    res["dynamic_beats_static"] = bool(res["dynamic"]["makespan_us"] < res["static"]["makespan_us"])
+    out["grouped_uneven"] = res
+    plan.destroy()
+    del As, Bs, Cs
+
+    # tail boundary: T = 255 / 256 / 257 tiles of 256 x 256, K = 4096
+    log("tail: boundary")
+    plan = ptg.gemm_create(tile_edge=256, log_capacity=512)
+    res = {}
+    for name in ("tail_255", "tail_256", "tail_257"):
+        q = make_workload(name).problems[0]
+        A = ptg.bf16_from_bits(q.a_bits)
+        B = ptg.bf16_from_bits(q.b_bits)
+        C = torch.empty((q.M, q.N), dtype=torch.float32, device="cuda")
+        r = {}
+        for mode in modes:
+            ms_ev = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream), 5, 2, stream)
+            ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
+            rec = ptg.gemm_read_log(plan)
+            ms = makespan_from_log(rec, khz)
+            ms["kernel_us"] = ms_ev * 1e3
+            ms["hbm_gbs"] = (q.M * q.K * 2 + q.K * q.N * 2 + q.M * q.N * 4) / (ms_ev * 1e-3) / 1e9
+            r[mode] = ms
+        res[name] = r
+        del A, B, C
+    out["tail_boundary"] = res
+    plan.destroy()
+
+    # worked example: 12 tiles of 128 x 128, at most 3 workers at once, static P = 4
+    log("tail: worked example")
+    q = make_workload("worked_example").problems[0]
+    A = ptg.bf16_from_bits(q.a_bits)
+    B = ptg.bf16_from_bits(q.b_bits)
+    C = torch.empty((q.M, q.N), dtype=torch.float32, device="cuda")
+    plan = ptg.gemm_create(tile_edge=128, log_capacity=64, max_concurrent=3, static_workers=4,
+                           min_lds_bytes=96 * 1024)
+    res = {}
+    for mode in modes:
+        for _ in range(3):
+            ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
+        rec = ptg.gemm_read_log(plan)
+        res[mode] = makespan_from_log(rec, khz)
+    t = res["dynamic"]["tile_median_us"]
+    for mode in modes:
+        res[mode]["makespan_t"] = res[mode]["makespan_us"] / t
+    res["static_over_dynamic"] = res["static"]["makespan_us"] / res["dynamic"]["makespan_us"]
+    res["pages_hand_calc_t"] = {"static": 6, "dynamic": 4, "nonpersistent": 4}
+    out["worked_example"] = res
+    plan.destroy()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", default="dynamic", choices=["nonpersistent", "static", "dynamic"])
+    ap.add_argument("--claims-ahead", type=int, default=1)
+    ap.add_argument("--raster-group", type=int, default=0, help="grouped-M raster height (0: row-major)")
+    ap.add_argument("--no-log", action="store_true", help="turn the tile log off")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tail", action="store_true")
+    ap.add_argument("--no-modes", action="store_true", help="skip timing the other schedulers")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times) to scale the HBM byte counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the single-GPU path is what is measured; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+        return
+    import persistent_tiled_gemm_amd as ptg
+    from workloads import make_workload
+
+    ptg.load_library()  # fails loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    log("generating square_8192 inputs")
+    w = make_workload("square_8192")
+    p = w.problems[0]
+    M, N, K = p.M, p.N, p.K
+    A = ptg.bf16_from_bits(p.a_bits)
+    B = ptg.bf16_from_bits(p.b_bits)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    fields = {"tile_edge": 256, "claims_ahead": args.claims_ahead, "log_capacity": 0 if args.no_log else 1024}
+    if args.raster_group > 1:
+        fields.update(raster=1, raster_group=args.raster_group)
+    plan = ptg.gemm_create(**fields)
+    info = ptg.gemm_plan_info_get(plan)
+    khz = info["wallclock_khz"]
+    flops = 2.0 * M * N * K
+
+    log(f"timing {args.mode}: warmup {args.warmup}, steps {args.steps}")
+    ms = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=args.mode, stream=stream), args.steps, args.warmup, stream)
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    modes = {}
+    if not args.no_modes:
+        for mode in ("nonpersistent", "static", "dynamic"):
+            m_ms = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream), max(5, args.steps // 2),
+                             2, stream)
+            ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
+            mk = makespan_from_log(ptg.gemm_read_log(plan), khz) if not args.no_log else None
+            modes[mode] = {"ms": m_ms, "tflops": flops / (m_ms * 1e-3) / 1e12,
+                           "frac_peak": flops / (m_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            if mk:
+                modes[mode].update(makespan_us=mk["makespan_us"], tile_median_us=mk["tile_median_us"])
+
+    # sampled parity of the timed output against the oracle (a few rows)
+    from oracle.gemm_ref import check_result, gemm_ref_rows, decode_bf16
+    ptg.gemm_run(A, B, C, plan, mode=args.mode, stream=stream)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 4095, 8191])
+    ref = gemm_ref_rows(p.a_bits, p.b_bits, rows)
+    amax = float(np.abs(decode_bf16(p.a_bits)).max())
+    bmax = float(np.abs(decode_bf16(p.b_bits)).max())
+    rep = check_result(C[rows.tolist()].cpu().numpy(), ref, K, amax, bmax)
+
+    roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(1.0),
+            "kernel": f"ptg_gemm_kernel<256,256,{args.mode}>", "avg_launch_ms": ms,
+            "algorithmic_flop_per_launch": flops}
+
+    out = {"metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "square_8192", "M": M, "N": N, "K": K, "tile": [256, 256, 64],
+                      "sched": args.mode, "claims_ahead": args.claims_ahead, "ring_depth": 3,
+                      "raster_group": args.raster_group, "tile_log": not args.no_log, "accumulate": "fp32",
+                      "output": "fp32"},
+           "frac_peak": tflops / PEAK_BF16_TFLOPS, "roofline": roof,
+           "parity_sample": {"ok": rep["ok"], "rel_frob": rep["rel_frob"], "rows": rows.tolist()},
+           "modes": modes}
+
+    if not args.no_tail:
+        out["tail"] = run_tail_sections(ptg, torch, stream, khz, (p, A, B, C))
+    plan.destroy()
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        out["cpu_baseline"] = cpu_baseline(p)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -80,8 +80,14 @@ typedef enum gemm_sched_mode {
  *   bm, bn, bk      output tile and K step: {128,128,64} or {256,256,64}.
  *   ring_depth      depth of the LDS ring of claim records: 3 (2..3 accepted).
  *   claims_ahead    throttle: how many claims a dynamic worker holds beyond its
- *                   current tile: 0 (claim after finishing), 1 (claim when a tile
- *                   starts) or 2; must be < ring_depth.
+ *                   current tile: 0 (claim after finishing the tile), 1 or 2;
+ *                   must be < ring_depth.
+ *   claim_lead      with claims_ahead >= 1, the claims for later tiles are issued
+ *                   at the start of k-step max(0, nk - claim_lead) of the current
+ *                   tile (nk = its number of 64-deep k-steps): late, so a worker
+ *                   does not take work a not-yet-started slot would get, yet
+ *                   early enough for the atomic's round trip to hide under the
+ *                   MFMAs. 0 = at the last k-step; >= nk = at the tile start.
  *   raster          0 = row-major tile order; 1 = grouped-M with group height
  *                   raster_group tile rows.
  *   static_workers  static mode's P; 0 = resident workgroups (occupancy x CUs).
@@ -96,6 +102,7 @@ typedef struct gemm_tile_desc {
   int32_t bm, bn, bk;
   int32_t ring_depth;
   int32_t claims_ahead;
+  int32_t claim_lead;
   int32_t raster;
   int32_t raster_group;
   int32_t static_workers;

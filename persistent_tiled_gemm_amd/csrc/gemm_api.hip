@@ -28,9 +28,10 @@ struct gemm_plan {
   int64_t wallclock_khz = 0;
   int lds_bytes = 0;
   int dyn_lds = 0;
-  // device scratch: [SchedCtrl][visits u32 x log_capacity] in one block, plus the log
+  // device scratch: two sets of [SchedCtrl][visits u32 x log_capacity], plus the log
   unsigned char *d_ctrl_block = nullptr;
-  size_t ctrl_block_bytes = 0;
+  size_t ctrl_set_bytes = 0;
+  uint64_t runs = 0;  // launches so far; run i uses set i % 2
   TileRecDev *d_log = nullptr;
   KernelProblem *d_groups = nullptr;
   KernelProblem *h_groups = nullptr;  // pinned staging for the grouped table
@@ -84,14 +85,7 @@ gemm_status check_current_device(gemm_plan *p) {
   return GEMM_OK;
 }
 
-// Clear the scheduler state (and the visit counters of the tiles to be logged).
-gemm_status reset_scratch(gemm_plan *p, int64_t tiles, hipStream_t s) {
-  size_t bytes = sizeof(SchedCtrl);
-  if (p->desc.log_capacity > 0) bytes += sizeof(uint32_t) * (size_t)std::min<int64_t>(tiles, p->desc.log_capacity);
-  hipError_t e = hipMemsetAsync(p->d_ctrl_block, 0, bytes, s);
-  if (e != hipSuccess) return hip_fail(p, e, "hipMemsetAsync(scratch)");
-  return GEMM_OK;
-}
+unsigned char *ctrl_set(gemm_plan *p, uint64_t run) { return p->d_ctrl_block + (run & 1u) * p->ctrl_set_bytes; }
 
 gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, int64_t tiles, hipStream_t s) {
   if (mode < GEMM_SCHED_NONPERSISTENT || mode > GEMM_SCHED_DYNAMIC) return GEMM_E_INVALID_ARG;
@@ -101,6 +95,7 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   args.P = (int32_t)grid;
   args.claims_ahead = p->desc.claims_ahead;
   args.ring_depth = p->desc.ring_depth;
+  args.claim_lead = p->desc.claim_lead;
   args.raster_group = p->desc.raster == 1 ? p->desc.raster_group : 1;
   args.counter_base = 0;
   if (mode == GEMM_SCHED_DYNAMIC && p->preset_pending) {
@@ -109,13 +104,16 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   }
   args.max_concurrent = p->desc.max_concurrent;
   args.log_cap = p->desc.log_capacity;
-  args.ctrl = reinterpret_cast<SchedCtrl *>(p->d_ctrl_block);
-  args.visits = reinterpret_cast<uint32_t *>(p->d_ctrl_block + sizeof(SchedCtrl));
+  unsigned char *cur = ctrl_set(p, p->runs), *nxt = ctrl_set(p, p->runs + 1);
+  args.ctrl = reinterpret_cast<SchedCtrl *>(cur);
+  args.visits = reinterpret_cast<uint32_t *>(cur + sizeof(SchedCtrl));
+  args.ctrl_next = reinterpret_cast<SchedCtrl *>(nxt);
+  args.visits_next = reinterpret_cast<uint32_t *>(nxt + sizeof(SchedCtrl));
+  args.clear_count = p->desc.log_capacity;
   args.log = p->d_log;
-  gemm_status st = reset_scratch(p, tiles, s);
-  if (st != GEMM_OK) return st;
   hipError_t e = ptg::launch_gemm(p->desc.bm, mode, grouped, args, (int)grid, p->dyn_lds, s);
   if (e != hipSuccess) return hip_fail(p, e, "kernel launch");
+  ++p->runs;
   p->last_stream = s;
   p->has_run = true;
   p->last_tiles = tiles;
@@ -151,6 +149,7 @@ gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t de
   out->bk = 64;
   out->ring_depth = 3;
   out->claims_ahead = 1;
+  out->claim_lead = 2;
   out->raster = 0;
   out->raster_group = 8;
   out->static_workers = 0;
@@ -169,6 +168,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (!valid_tile(d)) return GEMM_E_UNSUPPORTED;
   if (d.ring_depth < 2 || d.ring_depth > 3) return GEMM_E_INVALID_ARG;
   if (d.claims_ahead < 0 || d.claims_ahead > 2 || d.claims_ahead >= d.ring_depth) return GEMM_E_INVALID_ARG;
+  if (d.claim_lead < 0) return GEMM_E_INVALID_ARG;
   if (d.raster < 0 || d.raster > 1 || (d.raster == 1 && d.raster_group < 1)) return GEMM_E_INVALID_ARG;
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
       d.max_groups < 0)
@@ -210,12 +210,12 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   p->occupancy = occ;
   p->static_workers = d.static_workers > 0 ? d.static_workers : occ * p->cu_count;
 
-  p->ctrl_block_bytes = sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)std::max(d.log_capacity, 1);
-  if (hipMalloc(&p->d_ctrl_block, p->ctrl_block_bytes) != hipSuccess) {
+  p->ctrl_set_bytes = (sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)std::max(d.log_capacity, 1) + 255) & ~(size_t)255;
+  if (hipMalloc(&p->d_ctrl_block, 2 * p->ctrl_set_bytes) != hipSuccess) {
     delete p;
     return GEMM_E_NOMEM;
   }
-  if (hipMemset(p->d_ctrl_block, 0, p->ctrl_block_bytes) != hipSuccess) {
+  if (hipMemset(p->d_ctrl_block, 0, 2 * p->ctrl_set_bytes) != hipSuccess) {
     gemm_destroy(p);
     return GEMM_E_HIP;
   }
@@ -347,10 +347,11 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
   if (m > 0) {
     e = hipMemcpy(recs.data(), p->d_log, sizeof(TileRecDev) * m, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(log)");
-    e = hipMemcpy(visits.data(), p->d_ctrl_block + sizeof(SchedCtrl), sizeof(uint32_t) * m, hipMemcpyDeviceToHost);
+    e = hipMemcpy(visits.data(), ctrl_set(p, p->runs - 1) + sizeof(SchedCtrl), sizeof(uint32_t) * m,
+                  hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(visits)");
   }
-  e = hipMemcpy(&ctrl, p->d_ctrl_block, sizeof(ctrl), hipMemcpyDeviceToHost);
+  e = hipMemcpy(&ctrl, ctrl_set(p, p->runs - 1), sizeof(ctrl), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(ctrl)");
   for (size_t i = 0; i < m; ++i) {
     gemm_tile_rec &r = host_out[i];

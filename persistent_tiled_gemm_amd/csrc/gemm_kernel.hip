@@ -60,6 +60,18 @@ struct RingRec {
 static constexpr int kRingDepth = 3;  // LDS slots; a run uses args.ring_depth (2 or 3) of them
 static constexpr uint32_t kGateSpinLimit = 1u << 22;  // x ~1.7 us sleeps: a few seconds at most
 
+// Ask the scheduler for an alternation of one MFMA and one LDS read in the
+// current scheduling region (then the remaining MFMAs or reads).
+template <int READS, int MFMAS>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < MFMAS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+    if (i < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  if constexpr (READS > MFMAS) __builtin_amdgcn_sched_group_barrier(0x100, READS - MFMAS, 0);
+}
+
 __device__ __forceinline__ uint32_t claim_next(const KernelArgs &a) {
   return __hip_atomic_fetch_add(&a.ctrl->counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + a.counter_base;
 }
@@ -67,7 +79,7 @@ __device__ __forceinline__ uint32_t claim_next(const KernelArgs &a) {
 template <int BM, int BN, int MODE, bool GROUPED>
 __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args) {
   using CF = Cfg<BM, BN>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::LDS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::LDS];  // two stages
   __shared__ RingRec ring[kRingDepth];
   __shared__ uint32_t gate_ok;
 
@@ -76,6 +88,20 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
   const uint32_t wave = wave_uniform(tid >> 6);
   const uint32_t wm = wave >> 1, wn = wave & 1u;
   const int32_t T = args.T;
+
+  // ---- clear the next run's scheduler state (spread over the grid)
+  if (blockIdx.x == 0 && tid == 0) {
+    args.ctrl_next->counter = 0u;
+    args.ctrl_next->gate = 0u;
+    args.ctrl_next->error = 0u;
+  }
+  if (args.clear_count > 0) {
+    const uint32_t chunk = ((uint32_t)args.clear_count + gridDim.x - 1u) / gridDim.x;
+    const uint32_t first = blockIdx.x * chunk;
+    for (uint32_t i = tid; i < chunk; i += 256u) {
+      if (first + i < (uint32_t)args.clear_count) args.visits_next[first + i] = 0u;
+    }
+  }
 
   // ---- optional concurrency gate: at most max_concurrent workgroups compute at once
   if (args.max_concurrent > 0) {
@@ -132,6 +158,16 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
     if constexpr (GROUPED) {
       const int32_t g = find_problem(args.groups, args.G, (int32_t)tile);
       pb = args.groups[g];
+      // the descriptor is the same for the whole workgroup: keep it in SGPRs
+      pb.A = uniform_ptr(pb.A);
+      pb.B = uniform_ptr(pb.B);
+      pb.C = uniform_ptr(pb.C);
+      pb.M = (int32_t)wave_uniform((uint32_t)pb.M);
+      pb.N = (int32_t)wave_uniform((uint32_t)pb.N);
+      pb.K = (int32_t)wave_uniform((uint32_t)pb.K);
+      pb.tiles_m = (int32_t)wave_uniform((uint32_t)pb.tiles_m);
+      pb.tiles_n = (int32_t)wave_uniform((uint32_t)pb.tiles_n);
+      pb.tile_start = (int32_t)wave_uniform((uint32_t)pb.tile_start);
       local -= pb.tile_start;
     } else {
       pb = args.single;
@@ -150,61 +186,71 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
     // ---- claim ahead (the throttle: at most claims_ahead beyond the current tile)
     uint32_t batch[2] = {0u, 0u};
     uint32_t batch_ord = 0, batch_n = 0;
-    if constexpr (MODE == kDynamic) {
-      if (tid == 0 && !failed && args.claims_ahead >= 1) {
-        batch_ord = next_ord;
-        while (next_ord <= ord + (uint32_t)args.claims_ahead && batch_n < 2) {
-          batch[batch_n++] = claim_next(args);
-          ++next_ord;
+    auto do_claims = [&]() {
+      if constexpr (MODE == kDynamic) {
+        if (tid == 0 && !failed && args.claims_ahead >= 1) {
+          batch_ord = next_ord;
+          while (next_ord <= ord + (uint32_t)args.claims_ahead && batch_n < 2) {
+            batch[batch_n++] = claim_next(args);
+            ++next_ord;
+          }
         }
       }
-    }
+    };
 
-    // ---- per-thread load offsets for this tile (row / column edges masked)
-    uint32_t voff_a[CF::A_LOADS];
-    uint32_t kchunk_a[CF::A_LOADS];
-#pragma unroll
-    for (int j = 0; j < CF::A_LOADS; ++j) {
-      const uint32_t p = (uint32_t)(j * 4 + (int)wave) * 64u + lane;
-      const uint32_t row = p >> 3;
-      const uint32_t c = (p & 7u) ^ swz_a(row);
-      kchunk_a[j] = c * 8u;
-      voff_a[j] = (m0 + (int32_t)row < M) ? (row * (uint32_t)K + c * 8u) * 2u : kBufOob;
-    }
-    uint32_t voff_b[CF::B_LOADS];
-    uint32_t krow_b[CF::B_LOADS];
-#pragma unroll
-    for (int j = 0; j < CF::B_LOADS; ++j) {
-      const uint32_t p = (uint32_t)(j * 4 + (int)wave) * 64u + lane;
-      const uint32_t k = p / CF::B_ROW_CHUNKS;
-      const uint32_t c = (p % CF::B_ROW_CHUNKS) ^ swz_b(k);
-      krow_b[j] = k;
-      voff_b[j] = (n0 + (int32_t)(c * 8u) < N) ? (k * (uint32_t)N + c * 8u) * 2u : kBufOob;
-    }
+    // ---- per-thread load addressing for this tile. Load j of a wave moves a
+    // 1 KiB block: A rows (j*4+wave)*8 .. +8 (8 lanes per 128-byte row), B k rows
+    // (j*4+wave)*(64/B_ROW_CHUNKS*...) (B_ROW_CHUNKS lanes per row). The swizzle
+    // of A depends on j only through j's parity and that of B not at all, so the
+    // per-load voffset is one of two (A) or one (B) per-lane bases plus a
+    // wave-uniform step.
+    constexpr uint32_t kBRowsPerLoad = 64u / CF::B_ROW_CHUNKS;  // k rows one wave-load covers
+    const uint32_t a_row0 = wave * 8u + (lane >> 3);             // row of load j = a_row0 + 32 j
+    const uint32_t a_c_even = ((lane & 7u) ^ (lane >> 3) ^ wave) & 7u;
+    const uint32_t a_c_odd = a_c_even ^ 4u;
+    const uint32_t a_base_even = a_row0 * (uint32_t)K * 2u + a_c_even * 16u;
+    const uint32_t a_base_odd = a_row0 * (uint32_t)K * 2u + a_c_odd * 16u;
+    const uint32_t b_k0 = wave * kBRowsPerLoad + lane / CF::B_ROW_CHUNKS;  // k row of load j = b_k0 + 4*kBRowsPerLoad j
+    const uint32_t b_c = (lane % CF::B_ROW_CHUNKS) ^ swz_b(b_k0);
+    const bool b_col_ok = n0 + (int32_t)(b_c * 8u) < N;
+    const uint32_t b_base = b_col_ok ? (b_k0 * (uint32_t)N + b_c * 8u) * 2u : kBufOob;
+    const int32_t m_left = M - m0;  // rows of A that exist in this tile
     const uint16_t *a_tile = pb.A + (size_t)m0 * (size_t)K;
     const uint16_t *b_tile = pb.B + n0;
     const int32_t nk = (K + CF::BK - 1) / CF::BK;
     const int32_t full = K / CF::BK;  // k-steps with no K tail
 
-    auto issue_stage = [&](int st, int32_t kt) {
-      unsigned char *sa = smem + st * CF::STAGE;
-      unsigned char *sb = sa + CF::A_STAGE;
+    // voffset of load j (A loads first, then B) for k-step kt; chunks outside
+    // the matrix (row / column edges, K tail) read as zero via kBufOob.
+    auto load_voff = [&](int j, int32_t kt) -> uint32_t {
       const int32_t k0 = kt * CF::BK;
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + k0);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile + (size_t)k0 * (size_t)N);
       const bool tail = kt >= full;
-#pragma unroll
-      for (int j = 0; j < CF::A_LOADS; ++j) {
-        uint32_t vo = voff_a[j];
-        if (tail && k0 + (int32_t)kchunk_a[j] >= K) vo = kBufOob;
-        load16_to_lds(ra, sa + (j * 4 + (int)wave) * 1024, vo);
+      if (j < CF::A_LOADS) {
+        const uint32_t row = a_row0 + 32u * (uint32_t)j;
+        const uint32_t c = (j & 1) ? a_c_odd : a_c_even;
+        const uint32_t vo = ((j & 1) ? a_base_odd : a_base_even) + (uint32_t)j * 64u * (uint32_t)K;
+        const bool out = (int32_t)row >= m_left || (tail && k0 + (int32_t)(c * 8u) >= K);
+        return out ? kBufOob : vo;
       }
+      const int jb = j - CF::A_LOADS;
+      const uint32_t krow = b_k0 + 4u * kBRowsPerLoad * (uint32_t)jb;
+      const uint32_t vo = b_base + (uint32_t)jb * 4u * kBRowsPerLoad * (uint32_t)N * 2u;
+      const bool out = b_base == kBufOob || (tail && k0 + (int32_t)krow >= K);
+      return out ? kBufOob : vo;
+    };
+    auto load_dst = [&](int j) -> uint32_t {
+      return j < CF::A_LOADS ? (uint32_t)(j * 4 + (int)wave) * 1024u
+                             : (uint32_t)CF::A_STAGE + (uint32_t)((j - CF::A_LOADS) * 4 + (int)wave) * 1024u;
+    };
+    // all loads of k-step kt into stage dst, back to back (prologue)
+    auto issue_all = [&](int st, int32_t kt) {
+      unsigned char *dst = smem + st * CF::STAGE;
+      const i32x4 ra = make_rsrc_words(a_tile + kt * CF::BK);
+      const i32x4 rb = make_rsrc_words(b_tile + (size_t)(kt * CF::BK) * (size_t)N);
+      const uint32_t base = lds_addr(dst);
 #pragma unroll
-      for (int j = 0; j < CF::B_LOADS; ++j) {
-        uint32_t vo = voff_b[j];
-        if (tail && k0 + (int32_t)krow_b[j] >= K) vo = kBufOob;
-        load16_to_lds(rb, sb + (j * 4 + (int)wave) * 1024, vo);
-      }
+      for (int j = 0; j < CF::A_LOADS + CF::B_LOADS; ++j)
+        load16_to_lds(j < CF::A_LOADS ? ra : rb, base + load_dst(j), load_voff(j, kt));
     };
 
     // fragment read offsets (bytes inside a stage)
@@ -227,6 +273,56 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
       }
     }
 
+    // A fragment: 8 consecutive k of one row (ds_read_b128). B fragment: two
+    // transposing reads of 4 k each (ds_read_b64_tr_b16) for one column.
+    // Optionally, loads [first, first+count) of k-step kt_load into stage ldst
+    // are placed in program order between the reads; the reads alternate with
+    // MFMAs, so the loads land between MFMAs instead of in one burst.
+    auto read_frags = [&](int st, int s, bf16x8(&af)[CF::MI], bf16x8(&bfr)[CF::NI], int lst, int32_t kt_load,
+                          int first, int count) {
+      const unsigned char *sa = smem + st * CF::STAGE;
+      const unsigned char *sb = sa + CF::A_STAGE;
+      i32x4 ra = {0, 0, 0, 0}, rb = {0, 0, 0, 0};
+      uint32_t lbase = 0;
+      if (count > 0) {
+        ra = make_rsrc_words(a_tile + kt_load * CF::BK);
+        rb = make_rsrc_words(b_tile + (size_t)(kt_load * CF::BK) * (size_t)N);
+        lbase = lds_addr(smem + lst * CF::STAGE);
+      }
+#pragma unroll
+      for (int mi = 0; mi < CF::MI; ++mi) {
+        af[mi] = *(const bf16x8 *)(sa + off_a[mi] + ((((uint32_t)(2 * s)) ^ swa[mi]) << 4));
+        if (mi < count) {
+          const int j = first + mi;
+          load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
+        }
+      }
+#pragma unroll
+      for (int ni = 0; ni < CF::NI; ++ni) {
+        const unsigned char *pb0 = sb + off_b[ni] + (16 * s) * CF::B_ROW;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0));
+        if (CF::MI + 2 * ni < count) {
+          const int j = first + CF::MI + 2 * ni;
+          load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
+        }
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0 + 4 * CF::B_ROW));
+        if (CF::MI + 2 * ni + 1 < count) {
+          const int j = first + CF::MI + 2 * ni + 1;
+          load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
+        }
+        typedef __attribute__((ext_vector_type(8))) short i16x8;
+        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bfr[ni] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int r = CF::MI + 2 * CF::NI; r < CF::A_LOADS + CF::B_LOADS; ++r) {
+        if (r < count) {
+          const int j = first + r;
+          load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
+        }
+      }
+    };
+
     f32x16 acc[CF::MI][CF::NI];
 #pragma unroll
     for (int mi = 0; mi < CF::MI; ++mi)
@@ -235,56 +331,71 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
 
+    auto mma = [&](const bf16x8(&af)[CF::MI], const bf16x8(&bfr)[CF::NI]) {
+#pragma unroll
+      for (int mi = 0; mi < CF::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < CF::NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+    };
+
+    // the prefetch claim is issued claim_lead k-steps before the tile ends (the
+    // throttle): late enough not to take work a not-yet-started slot would get,
+    // early enough for the atomic's round trip to hide under the MFMAs
+    const int32_t claim_at = nk > args.claim_lead ? nk - args.claim_lead : 0;
+    if (nk == 0) do_claims();
+
     if (nk > 0) {
-      issue_stage(0, 0);
+      constexpr int kLoads = CF::A_LOADS + CF::B_LOADS;
+      constexpr int kReads = CF::MI + 2 * CF::NI;
+      constexpr int kMfma = CF::MI * CF::NI;
+      issue_all(0, 0);
       wait_vmem_all();
       wg_barrier();
+      bf16x8 a0[CF::MI], b0[CF::NI], a1[CF::MI], b1[CF::NI];
+      read_frags(0, 0, a0, b0, 0, 0, 0, 0);
       for (int32_t kt = 0; kt < nk; ++kt) {
+        // k-step kt on stage st while k-step kt+1 streams into stage st^1 (the
+        // last k-step reloads its own data instead, so no load is out of range);
+        // the loads are spread over the first two k-slices, between MFMAs
         const int st = kt & 1;
-        if (kt + 1 < nk) issue_stage(st ^ 1, kt + 1);
-        const unsigned char *sa = smem + st * CF::STAGE;
-        const unsigned char *sb = sa + CF::A_STAGE;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8 af[CF::MI];
-          bf16x8 bfr[CF::NI];
-#pragma unroll
-          for (int mi = 0; mi < CF::MI; ++mi)
-            af[mi] = *(const bf16x8 *)(sa + off_a[mi] + ((((uint32_t)(2 * s)) ^ swa[mi]) << 4));
-#pragma unroll
-          for (int ni = 0; ni < CF::NI; ++ni) {
-            const unsigned char *pb0 = sb + off_b[ni] + (16 * s) * CF::B_ROW;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0 + 4 * CF::B_ROW));
-            typedef __attribute__((ext_vector_type(8))) short i16x8;
-            const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            bfr[ni] = __builtin_bit_cast(bf16x8, v);
-          }
-#pragma unroll
-          for (int mi = 0; mi < CF::MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < CF::NI; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-        }
+        if (kt == claim_at) do_claims();
+        const int32_t kl = kt + 1 < nk ? kt + 1 : kt;
+        read_frags(st, 1, a1, b1, st ^ 1, kl, 0, kLoads / 2);
+        mma(a0, b0);
+        interleave<kReads, kMfma>();
+        read_frags(st, 2, a0, b0, st ^ 1, kl, kLoads / 2, kLoads - kLoads / 2);
+        mma(a1, b1);
+        interleave<kReads, kMfma>();
+        read_frags(st, 3, a1, b1, 0, 0, 0, 0);
+        mma(a0, b0);
+        interleave<kReads, kMfma>();
+        // stage st fully read and stage st^1 landed: publish it to every wave
+        wait_lds_all();
         wait_vmem_all();
         wg_barrier();
+        // slice 3 runs while slice 0 of the next stage is read (after the last
+        // k-step these values are never used)
+        read_frags(st ^ 1, 0, a0, b0, 0, 0, 0, 0);
+        mma(a1, b1);
+        interleave<kReads, kMfma>();
       }
     }
 
     // ---- epilogue: fp32 accumulators -> C (lane holds 4 consecutive n of one m)
+    const bool interior = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
     for (int mi = 0; mi < CF::MI; ++mi) {
       const int32_t m = m0 + (int32_t)(wm * CF::WM + mi * 32 + (lane & 31u));
+      float *crow = pb.C + (size_t)m * (size_t)N;
 #pragma unroll
       for (int ni = 0; ni < CF::NI; ++ni) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const int32_t n = n0 + (int32_t)(wn * CF::WN + ni * 32 + 8 * qd + 4 * (lane >> 5));
-          if (m < M && n < N) {
-            f32x4 v = {acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1], acc[mi][ni][4 * qd + 2],
-                       acc[mi][ni][4 * qd + 3]};
-            *(f32x4 *)(pb.C + (size_t)m * (size_t)N + n) = v;
-          }
+          const f32x4 v = {acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1], acc[mi][ni][4 * qd + 2],
+                           acc[mi][ni][4 * qd + 3]};
+          if (interior || (m < M && n < N)) *(f32x4 *)(crow + n) = v;
         }
       }
     }

@@ -28,11 +28,48 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)kBufRecords, 0x00020000);
 }
 
-// 16 bytes per lane from global memory straight into LDS at lds_base + lane*16
-// (lds_base is wave-uniform; it goes to M0).
-__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void *lds_base, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)lds_base, 16, voffset, 0, 0, 0);
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// The same resource as four SGPR words, for inline assembly (the base must be
+// wave-uniform; readfirstlane makes that explicit to the compiler).
+__device__ __forceinline__ i32x4 make_rsrc_words(const void *base) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));  // stride 0
+  r[2] = (int)kBufRecords;
+  r[3] = 0x00020000;
+  return r;
 }
+
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + lane*16
+// (lds_base is wave-uniform; it goes to M0). Issued as inline assembly so the
+// compiler does not add a conservative wait before every later LDS read: the
+// kernel waits for these loads itself (vmcnt) before the barrier that
+// publishes the stage.
+__device__ __forceinline__ void load16_to_lds(i32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %0, %2, 0 offen lds"
+      :
+      : "v"(voffset), "s"(lds_base), "s"(rsrc)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_lds_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

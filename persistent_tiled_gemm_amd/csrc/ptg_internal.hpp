@@ -17,11 +17,13 @@ struct KernelProblem {
   int32_t tile_start;  // first global tile id of this problem
 };
 
-// Scheduler state in device memory, cleared before every run that uses it.
+// Scheduler state in device memory. A plan keeps two sets (control block +
+// visit counters); run i uses set i % 2 and clears set (i + 1) % 2 for the next
+// run, so a run is exactly one kernel launch with no host-side reset.
 struct alignas(64) SchedCtrl {
   uint32_t counter;    // dynamic claim counter
   uint32_t gate;       // workgroups currently holding a concurrency slot
-  uint32_t error;      // bit 0: a gate wait ran out
+  uint32_t error;      // bit 0: a gate wait ran out; bit 1: ring record for the wrong ordinal
   uint32_t pad[13];
 };
 
@@ -40,13 +42,17 @@ struct KernelArgs {
   int32_t P;                    // static stride (grid size of a static run)
   int32_t claims_ahead;         // 0, 1 or 2 (< ring_depth)
   int32_t ring_depth;           // 2 or 3
+  int32_t claim_lead;           // prefetch claims are issued this many k-steps before a tile ends
   int32_t raster_group;         // <= 1: row-major
   uint32_t counter_base;        // added to every claim (failure forcing)
   int32_t max_concurrent;       // 0: no gate
   int32_t log_cap;              // tiles logged (0: none)
-  SchedCtrl *ctrl;
+  SchedCtrl *ctrl;              // this run's set
   TileRecDev *log;
   uint32_t *visits;
+  SchedCtrl *ctrl_next;         // the next run's set, cleared by this run
+  uint32_t *visits_next;
+  int32_t clear_count;          // visit counters to clear in the next set
 };
 
 enum SchedMode { kNonPersistent = 0, kStatic = 1, kDynamic = 2 };
