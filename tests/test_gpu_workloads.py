@@ -1,0 +1,187 @@
+"""GPU parity at the full sizes of the measured workloads, in the launch
+configuration the benchmark times (256x256x64 tiles, claims-ahead 1, ring depth
+3, tile log on). Outputs are checked against the oracle on sampled rows (the
+oracle computes them row by row); ownership is checked bit-exactly on the log.
+"""
+
+import numpy as np
+import pytest
+
+import persistent_tiled_gemm_amd as ptg
+from oracle.gemm_ref import check_result, decode_bf16, gemm_ref_rows
+from oracle.ownership import check_ownership
+from tests.gpu_util import check_log, maxabs, say, torch_mod
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("nonpersistent", "static", "dynamic")
+
+
+def _sample_rows(M, tile, rng, per_tile_row=2):
+    rows = []
+    for t in range(-(-M // tile)):
+        lo, hi = t * tile, min(M, (t + 1) * tile)
+        rows += rng.integers(lo, hi, size=per_tile_row).tolist()
+    rows += [0, M - 1]
+    return np.array(sorted(set(rows)))
+
+
+def _check_rows(p, c, rows):
+    ref = gemm_ref_rows(p.a_bits, p.b_bits, rows)
+    rep = check_result(c[rows], ref, p.K, maxabs(p.a_bits), maxabs(p.b_bits))
+    assert rep["ok"], rep
+
+
+@pytest.fixture(scope="module")
+def square():
+    w = make_workload("square_8192")
+    p = w.problems[0]
+    return p, ptg.bf16_from_bits(p.a_bits), ptg.bf16_from_bits(p.b_bits)
+
+
+def test_square_8192_all_modes(square):
+    torch = torch_mod()
+    p, A, B = square
+    C = torch.empty((p.M, p.N), dtype=torch.float32, device="cuda")
+    plan = ptg.gemm_create(tile_edge=256, log_capacity=1024)
+    rows = _sample_rows(p.M, 256, np.random.default_rng(1), per_tile_row=1)
+    outs = {}
+    for mode in MODES:
+        say(f"case square_8192 mode={mode}")
+        C.fill_(float("nan"))
+        ptg.gemm_run(A, B, C, plan, mode=mode)
+        torch.cuda.synchronize()
+        info = ptg.gemm_plan_info_get(plan)
+        check_log(plan, mode, 1024, P=info["last_grid"] if mode == "static" else None)
+        c = C[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+        full = np.full((p.M, p.N), np.nan, dtype=np.float32)
+        full[rows] = c
+        _check_rows(p, full, rows)
+        outs[mode] = c
+        assert not torch.isnan(C).any().item()
+    assert np.array_equal(outs["dynamic"], outs["static"])
+    assert np.array_equal(outs["dynamic"], outs["nonpersistent"])
+    plan.destroy()
+
+
+@pytest.mark.parametrize("name,T", [("tail_255", 255), ("tail_256", 256), ("tail_257", 257)])
+def test_tail_boundary(name, T):
+    torch = torch_mod()
+    p = make_workload(name).problems[0]
+    A, B = ptg.bf16_from_bits(p.a_bits), ptg.bf16_from_bits(p.b_bits)
+    C = torch.empty((p.M, p.N), dtype=torch.float32, device="cuda")
+    plan = ptg.gemm_create(tile_edge=256, log_capacity=512)
+    rows = _sample_rows(p.M, 256, np.random.default_rng(T), per_tile_row=1)
+    for mode in MODES:
+        say(f"case {name} mode={mode}")
+        C.fill_(float("nan"))
+        ptg.gemm_run(A, B, C, plan, mode=mode)
+        torch.cuda.synchronize()
+        info = ptg.gemm_plan_info_get(plan)
+        log = check_log(plan, mode, T, P=info["last_grid"] if mode == "static" else None)
+        if mode == "static":
+            assert info["last_grid"] == min(T, info["static_workers"])
+        full = C.cpu().numpy()
+        assert not np.isnan(full).any()
+        _check_rows(p, full, rows)
+    plan.destroy()
+
+
+def test_grouped_uneven_all_modes():
+    torch = torch_mod()
+    w = make_workload("grouped_uneven")
+    As = [ptg.bf16_from_bits(q.a_bits) for q in w.problems]
+    Bs = [ptg.bf16_from_bits(q.b_bits) for q in w.problems]
+    Cs = [torch.empty((q.M, q.N), dtype=torch.float32, device="cuda") for q in w.problems]
+    plan = ptg.gemm_create(tile_edge=256, log_capacity=1024)
+    rng = np.random.default_rng(3)
+    for mode in MODES:
+        say(f"case grouped_uneven mode={mode}")
+        for c in Cs:
+            c.fill_(float("nan"))
+        ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode)
+        torch.cuda.synchronize()
+        info = ptg.gemm_plan_info_get(plan)
+        log = check_log(plan, mode, 1024, P=info["last_grid"] if mode == "static" else None)
+        # the log's problem index matches the tile numbering (16 tiles per problem)
+        assert np.array_equal(log["problem"], np.arange(1024) // 16)
+        for g in range(0, 64, 7):
+            q = w.problems[g]
+            full = Cs[g].cpu().numpy()
+            assert not np.isnan(full).any()
+            _check_rows(q, full, _sample_rows(q.M, 256, rng, per_tile_row=1))
+    plan.destroy()
+
+
+def test_partial_occupancy_co_run(square):
+    """The 8192^3 GEMM co-run with a spoiler holding 64 CUs for 2 ms: results stay
+    exact, the spoiler occupies 64 distinct CUs, and no GEMM tile runs on a
+    spoiled CU while its spoiler workgroup is still spinning."""
+    torch = torch_mod()
+    p, A, B = square
+    C = torch.empty((p.M, p.N), dtype=torch.float32, device="cuda")
+    plan = ptg.gemm_create(tile_edge=256, log_capacity=1024)
+    khz = ptg.gemm_plan_info_get(plan)["wallclock_khz"]
+    spoil = torch.cuda.Stream()
+    rows = _sample_rows(p.M, 256, np.random.default_rng(5), per_tile_row=1)
+    for mode in ("static", "dynamic"):
+        say(f"case partial_occupancy mode={mode}")
+        slog = torch.zeros(64 * 4, dtype=torch.int64, device="cuda")
+        C.fill_(float("nan"))
+        ptg.gemm_spoiler_run(64, 2_000_000, stream=spoil, log=slog, wait_resident_ms=2000.0)
+        ptg.gemm_run(A, B, C, plan, mode=mode)
+        torch.cuda.synchronize()
+        info = ptg.gemm_plan_info_get(plan)
+        log = check_log(plan, mode, 1024, P=info["last_grid"] if mode == "static" else None)
+        full = C.cpu().numpy()
+        assert not np.isnan(full).any()
+        _check_rows(p, full, rows[::4])
+        sl = slog.cpu().numpy().reshape(64, 4)
+        key = lambda hw, xcc: (np.asarray(xcc, np.int64) << 8) | ((np.asarray(hw, np.int64) >> 8) & 0xFF)
+        spoiled = key(sl[:, 2], sl[:, 3])
+        assert len(np.unique(spoiled)) == 64
+        assert (sl[:, 1] - sl[:, 0]).min() >= 2_000_000 * khz / 1e6 * 0.999  # each spun its 2 ms
+        tiles_cu = key(log["hw_id"], log["xcc_id"])
+        for s in range(64):
+            on_cu = tiles_cu == spoiled[s]
+            # a tile on this CU may not overlap the spoiler's residency there
+            overl = (log["r0"][on_cu] < sl[s, 1]) & (log["r1"][on_cu] > sl[s, 0])
+            assert not overl.any(), (mode, s)
+    plan.destroy()
+
+
+def test_worked_example_concurrency_cap():
+    """12 tiles of 128 x 128, at most 3 workers at once, static P = 4: the log shows
+    at most 3 tiles in flight at any moment and the static makespan exceeds the
+    dynamic one (the pages' 6t vs 4t; the exact ratio is a hardware fact)."""
+    torch = torch_mod()
+    p = make_workload("worked_example").problems[0]
+    A, B = ptg.bf16_from_bits(p.a_bits), ptg.bf16_from_bits(p.b_bits)
+    C = torch.empty((p.M, p.N), dtype=torch.float32, device="cuda")
+    plan = ptg.gemm_create(tile_edge=128, log_capacity=64, max_concurrent=3, static_workers=4,
+                           min_lds_bytes=96 * 1024)
+    spans = {}
+    for mode in MODES:
+        say(f"case worked_example mode={mode}")
+        for _ in range(3):
+            C.fill_(float("nan"))
+            ptg.gemm_run(A, B, C, plan, mode=mode)
+        torch.cuda.synchronize()
+        info = ptg.gemm_plan_info_get(plan)
+        log = check_log(plan, mode, 12, P=4 if mode == "static" else None)
+        ev = sorted([(int(r), 1) for r in log["r0"]] + [(int(r), -1) for r in log["r1"]], key=lambda e: (e[0], e[1]))
+        live = peak = 0
+        for _, d in ev:
+            live += d
+            peak = max(peak, live)
+        assert peak <= 3, (mode, peak)
+        if mode == "dynamic":
+            assert len(np.unique(log["worker"])) <= 3
+        if mode == "static":
+            for w in range(4):
+                assert sorted(log["tile"][log["worker"] == w].tolist()) == [w, w + 4, w + 8]
+        _check_rows(p, C.cpu().numpy(), np.arange(p.M))
+        spans[mode] = float(log["r1"].max() - log["r0"].min())
+    assert spans["static"] > 1.15 * spans["dynamic"], spans
+    plan.destroy()
