@@ -239,6 +239,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mode", default="dynamic", choices=["nonpersistent", "static", "dynamic"])
     ap.add_argument("--claims-ahead", type=int, default=1)
+    ap.add_argument("--claim-policy", type=int, default=1, choices=[0, 1],
+                    help="0: one device-wide claim counter; 1: per-XCD counters with stealing")
     ap.add_argument("--raster-group", type=int, default=0, help="grouped-M raster height (0: row-major)")
     ap.add_argument("--no-log", action="store_true", help="turn the tile log off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -278,7 +280,8 @@ def main():
     A = ptg.bf16_from_bits(p.a_bits)
     B = ptg.bf16_from_bits(p.b_bits)
     C = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    fields = {"tile_edge": 256, "claims_ahead": args.claims_ahead, "log_capacity": 0 if args.no_log else 1024}
+    fields = {"tile_edge": 256, "claims_ahead": args.claims_ahead, "claim_policy": args.claim_policy,
+              "log_capacity": 0 if args.no_log else 1024}
     if args.raster_group > 1:
         fields.update(raster=1, raster_group=args.raster_group)
     plan = ptg.gemm_create(**fields)
@@ -292,15 +295,20 @@ def main():
 
     modes = {}
     if not args.no_modes:
-        for mode in ("nonpersistent", "static", "dynamic"):
-            m_ms = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream), max(5, args.steps // 2),
+        other = dict(fields, claim_policy=1 - args.claim_policy)
+        plan_other = ptg.gemm_create(**other)
+        runs = [("nonpersistent", "nonpersistent", plan), ("static", "static", plan), ("dynamic", "dynamic", plan),
+                ("dynamic_single_counter" if args.claim_policy == 1 else "dynamic_xcd_counters", "dynamic", plan_other)]
+        for name, mode, pl in runs:
+            m_ms = time_runs(lambda: ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream), max(5, args.steps // 2),
                              2, stream)
-            ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
-            mk = makespan_from_log(ptg.gemm_read_log(plan), khz) if not args.no_log else None
-            modes[mode] = {"ms": m_ms, "tflops": flops / (m_ms * 1e-3) / 1e12,
+            ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream)
+            mk = makespan_from_log(ptg.gemm_read_log(pl), khz) if not args.no_log else None
+            modes[name] = {"ms": m_ms, "tflops": flops / (m_ms * 1e-3) / 1e12,
                            "frac_peak": flops / (m_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
             if mk:
-                modes[mode].update(makespan_us=mk["makespan_us"], tile_median_us=mk["tile_median_us"])
+                modes[name].update(makespan_us=mk["makespan_us"], tile_median_us=mk["tile_median_us"])
+        plan_other.destroy()
 
     # sampled parity of the timed output against the oracle (a few rows)
     from oracle.gemm_ref import check_result, gemm_ref_rows, decode_bf16
@@ -321,7 +329,8 @@ def main():
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "square_8192", "M": M, "N": N, "K": K, "tile": [256, 256, 64],
-                      "sched": args.mode, "claims_ahead": args.claims_ahead, "ring_depth": 3,
+                      "sched": args.mode, "claim_policy": "xcd_counters" if args.claim_policy == 1 else "single_counter",
+                      "claims_ahead": args.claims_ahead, "ring_depth": 3,
                       "raster_group": args.raster_group, "tile_log": not args.no_log, "accumulate": "fp32",
                       "output": "fp32"},
            "frac_peak": tflops / PEAK_BF16_TFLOPS, "roofline": roof,

@@ -88,6 +88,14 @@ typedef enum gemm_sched_mode {
  *                   does not take work a not-yet-started slot would get, yet
  *                   early enough for the atomic's round trip to hide under the
  *                   MFMAs. 0 = at the last k-step; >= nk = at the tile start.
+ *   claim_policy    0 = one device-wide counter hands out tile ids in order.
+ *                   1 = XCD-partitioned: tile ids with id mod 8 == x form region
+ *                   x, handed out by counter x; a worker claims from the region
+ *                   of the XCD it runs on and, when that is exhausted, steals
+ *                   from the other regions. Every tile still has one owner; a
+ *                   worker's own-region tiles keep their L2 locality. The
+ *                   failure-forcing preset (gemm_test_preset_counter) applies
+ *                   to policy 0 only.
  *   raster          0 = row-major tile order; 1 = grouped-M with group height
  *                   raster_group tile rows.
  *   static_workers  static mode's P; 0 = resident workgroups (occupancy x CUs).
@@ -103,6 +111,7 @@ typedef struct gemm_tile_desc {
   int32_t ring_depth;
   int32_t claims_ahead;
   int32_t claim_lead;
+  int32_t claim_policy;
   int32_t raster;
   int32_t raster_group;
   int32_t static_workers;

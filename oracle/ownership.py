@@ -18,7 +18,9 @@ any worker finished that tile. The rules:
   ([CLC], section "why a fixed task sequence tails": W_i = i, i+4, i+8 for P = 4).
 * Dynamic: any exactly-once owner map is valid (the claim order decides it);
   because claims come from one monotone counter each worker's tiles are
-  strictly increasing in both id and start time.
+  strictly increasing in both id and start time. When tile ids are handed out
+  by several counters, one per region of ids (tile mod `regions`), the ids a
+  worker takes from any one region are strictly increasing.
 
 Timestamps are taken on the GPU's constant-rate clock; makespan = latest tile
 end - earliest tile start over the tiles that ran.
@@ -48,7 +50,7 @@ def makespan(start: np.ndarray, end: np.ndarray) -> float:
 
 def check_ownership(mode: str, T: int, tile: np.ndarray, worker: np.ndarray, start: np.ndarray,
                     end: np.ndarray, visits: np.ndarray, P: Optional[int] = None,
-                    expected_tiles: Optional[Iterable[int]] = None) -> List[str]:
+                    expected_tiles: Optional[Iterable[int]] = None, regions: int = 1) -> List[str]:
     """Return a list of violations (empty when the log obeys every rule).
 
     ``tile``, ``worker``, ``start``, ``end`` are per-record arrays for the tiles that
@@ -91,8 +93,14 @@ def check_ownership(mode: str, T: int, tile: np.ndarray, worker: np.ndarray, sta
         en = end[idx]
         if len(idx) > 1 and np.any(st[1:] < en[:-1]):
             errs.append(f"worker {w} runs two tiles at once")
-        if mode in ("static", "dynamic") and len(ks) > 1 and np.any(np.diff(ks) <= 0):
-            errs.append(f"worker {w} tiles not increasing in start order: {ks[:8].tolist()}")
+        if mode == "static" or (mode == "dynamic" and regions <= 1):
+            if len(ks) > 1 and np.any(np.diff(ks) <= 0):
+                errs.append(f"worker {w} tiles not increasing in start order: {ks[:8].tolist()}")
+        elif mode == "dynamic":
+            for r in range(regions):
+                kr = ks[ks % regions == r]
+                if len(kr) > 1 and np.any(np.diff(kr) <= 0):
+                    errs.append(f"worker {w} tiles of region {r} not increasing: {kr[:8].tolist()}")
     if mode == "nonpersistent":
         if np.any(worker != tile):
             errs.append("non-persistent owner(k) != k")

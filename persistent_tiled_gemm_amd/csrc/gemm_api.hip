@@ -96,6 +96,7 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   args.claims_ahead = p->desc.claims_ahead;
   args.ring_depth = p->desc.ring_depth;
   args.claim_lead = p->desc.claim_lead;
+  args.claim_policy = p->desc.claim_policy;
   args.raster_group = p->desc.raster == 1 ? p->desc.raster_group : 1;
   args.counter_base = 0;
   if (mode == GEMM_SCHED_DYNAMIC && p->preset_pending) {
@@ -150,6 +151,7 @@ gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t de
   out->ring_depth = 3;
   out->claims_ahead = 1;
   out->claim_lead = 2;
+  out->claim_policy = 1;
   out->raster = 0;
   out->raster_group = 8;
   out->static_workers = 0;
@@ -168,7 +170,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (!valid_tile(d)) return GEMM_E_UNSUPPORTED;
   if (d.ring_depth < 2 || d.ring_depth > 3) return GEMM_E_INVALID_ARG;
   if (d.claims_ahead < 0 || d.claims_ahead > 2 || d.claims_ahead >= d.ring_depth) return GEMM_E_INVALID_ARG;
-  if (d.claim_lead < 0) return GEMM_E_INVALID_ARG;
+  if (d.claim_lead < 0 || d.claim_policy < 0 || d.claim_policy > 1) return GEMM_E_INVALID_ARG;
   if (d.raster < 0 || d.raster > 1 || (d.raster == 1 && d.raster_group < 1)) return GEMM_E_INVALID_ARG;
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
       d.max_groups < 0)

@@ -1,8 +1,8 @@
 // Persistent tiled bf16 GEMM for gfx950: C (fp32) = A (bf16, M x K) . B (bf16, K x N).
 //
-// One workgroup = 4 wave64s in a 2 x 2 arrangement; each wave owns a
-// (BM/2) x (BN/2) block of the output tile and accumulates it in fp32 with
-// v_mfma_f32_32x32x16_bf16. Operand tiles move global -> LDS with
+// One workgroup = a grid of wave64s (2 x 2 for 128 x 128 tiles, 2 x 4 for
+// 256 x 256 tiles, i.e. two waves per SIMD); each wave owns a block of the
+// output tile and accumulates it in fp32 with v_mfma_f32_32x32x16_bf16. Operand tiles move global -> LDS with
 // buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR round trip) into two
 // LDS stages, so the loads of k-step kt+1 overlap the MFMAs of k-step kt.
 //
@@ -32,20 +32,41 @@
 
 namespace ptg {
 
-template <int BM, int BN>
+// Tile shape and wave grid. A workgroup has WAVES_M x WAVES_N wave64s; each
+// wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of the output tile.
+template <int BM, int BN, int WAVES_M, int WAVES_N>
 struct Cfg {
+  static constexpr int BM_ = BM, BN_ = BN, WAVES_N_ = WAVES_N;
+  static constexpr int NW = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int BK = 64;
-  static constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
-  static constexpr int MI = WM / 32, NI = WN / 32;  // 32x32 MFMA blocks per wave
-  static constexpr int A_LOADS = BM / 32;           // 16-byte loads per thread per stage
-  static constexpr int B_LOADS = BN / 32;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
+  static constexpr int MI = WM / 32, NI = WN / 32;            // 32x32 MFMA blocks per wave
+  static constexpr int A_LOADS = BM * (BK / 8) / THREADS;     // 16-byte loads per thread per stage
+  static constexpr int B_LOADS = BK * (BN / 8) / THREADS;
   static constexpr int A_STAGE = BM * BK * 2;       // bytes
   static constexpr int B_STAGE = BK * BN * 2;
   static constexpr int B_ROW = BN * 2;              // bytes per k row of the B stage
   static constexpr int B_ROW_CHUNKS = BN / 8;
   static constexpr int STAGE = A_STAGE + B_STAGE;
   static constexpr int LDS = 2 * STAGE;
+  static_assert(A_LOADS * THREADS == BM * (BK / 8) && B_LOADS * THREADS == BK * (BN / 8), "load split");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
 };
+
+// The wave grid used for each tile edge: 128 -> 2 x 2 waves (64 x 64 each);
+// 256 -> 2 x 4 waves (128 x 64 each), i.e. two waves per SIMD, so one wave's
+// MFMAs can issue while the other waits to issue its memory instructions.
+template <int EDGE> struct TileCfg;
+template <> struct TileCfg<128> { using type = Cfg<128, 128, 2, 2>; };
+#ifndef PTG_WAVES_256
+#define PTG_WAVES_256 8
+#endif
+#if PTG_WAVES_256 == 8
+template <> struct TileCfg<256> { using type = Cfg<256, 256, 2, 4>; };
+#else
+template <> struct TileCfg<256> { using type = Cfg<256, 256, 2, 2>; };
+#endif
 
 __device__ __forceinline__ uint32_t swz_a(uint32_t row) { return (row ^ (row >> 3)) & 7u; }
 __device__ __forceinline__ uint32_t swz_b(uint32_t k) { return 10u * (k & 1u) + 4u * ((k >> 1) & 1u); }
@@ -72,13 +93,34 @@ __device__ __forceinline__ void interleave() {
   if constexpr (READS > MFMAS) __builtin_amdgcn_sched_group_barrier(0x100, READS - MFMAS, 0);
 }
 
-__device__ __forceinline__ uint32_t claim_next(const KernelArgs &a) {
-  return __hip_atomic_fetch_add(&a.ctrl->counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + a.counter_base;
+// One claim. Single-counter policy: the next value of the device-wide counter
+// (plus the failure-forcing base); any value >= T is a failure. XCD-partitioned
+// policy: region x (tiles 8i + x) is handed out by counter x; a worker claims
+// from its own XCD's region first (the tiles its XCD's L2 already holds
+// operands for) and, once that is exhausted, steals from the other regions in
+// turn. Each counter returns each index once, so every tile still has exactly
+// one owner; the claim fails (returns T) only when every region is exhausted.
+// A relaxed load first skips regions already seen exhausted (counters only
+// grow, so a stale value can only under-report).
+__device__ __forceinline__ uint32_t claim_next(const KernelArgs &a, uint32_t xcc) {
+  if (a.claim_policy == 0)
+    return __hip_atomic_fetch_add(&a.ctrl->counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + a.counter_base;
+  const uint32_t T = (uint32_t)a.T;
+  for (uint32_t r = 0; r < (uint32_t)kXcdRegions; ++r) {
+    const uint32_t y = (xcc + r) % (uint32_t)kXcdRegions;
+    const uint32_t size = T > y ? (T - y + kXcdRegions - 1) / kXcdRegions : 0u;
+    uint32_t *ctr = &a.ctrl->xcd_counter[y];
+    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= size) continue;
+    const uint32_t i = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (i < size) return i * (uint32_t)kXcdRegions + y;
+  }
+  return T;
 }
 
 template <int BM, int BN, int MODE, bool GROUPED>
-__global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args) {
-  using CF = Cfg<BM, BN>;
+__global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel(const KernelArgs args) {
+  using CF = typename TileCfg<BM>::type;
+  static_assert(CF::BM_ == BM && CF::BN_ == BN, "config");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::LDS];  // two stages
   __shared__ RingRec ring[kRingDepth];
   __shared__ uint32_t gate_ok;
@@ -86,7 +128,7 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
   const uint32_t wave = wave_uniform(tid >> 6);
-  const uint32_t wm = wave >> 1, wn = wave & 1u;
+  const uint32_t wm = wave / (uint32_t)CF::WAVES_N_, wn = wave % (uint32_t)CF::WAVES_N_;
   const int32_t T = args.T;
 
   // ---- clear the next run's scheduler state (spread over the grid)
@@ -94,11 +136,12 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
     args.ctrl_next->counter = 0u;
     args.ctrl_next->gate = 0u;
     args.ctrl_next->error = 0u;
+    for (int x = 0; x < kXcdRegions; ++x) args.ctrl_next->xcd_counter[x] = 0u;
   }
   if (args.clear_count > 0) {
     const uint32_t chunk = ((uint32_t)args.clear_count + gridDim.x - 1u) / gridDim.x;
     const uint32_t first = blockIdx.x * chunk;
-    for (uint32_t i = tid; i < chunk; i += 256u) {
+    for (uint32_t i = tid; i < chunk; i += (uint32_t)CF::THREADS) {
       if (first + i < (uint32_t)args.clear_count) args.visits_next[first + i] = 0u;
     }
   }
@@ -124,6 +167,12 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
     if (!gate_ok) return;
   }
 
+  uint32_t hwid = 0, xcc = 0;
+  if (tid == 0) {
+    hwid = read_hw_id();
+    xcc = read_xcc_id() % (uint32_t)kXcdRegions;
+  }
+
   // ---- first tile
   uint32_t ord = 0;       // this worker's tile ordinal
   uint32_t tile = 0;
@@ -132,7 +181,7 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
   bool failed = false;    // producer: a claim has come back invalid
   if constexpr (MODE == kDynamic) {
     if (tid == 0) {
-      const uint32_t v = claim_next(args);
+      const uint32_t v = claim_next(args, xcc);
       const uint32_t ok = v < (uint32_t)T ? 1u : 0u;
       ring[0] = RingRec{v, ok, 0u, 0u};
       failed = !ok;
@@ -143,12 +192,6 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
   } else {
     tile = blockIdx.x;
     valid = tile < (uint32_t)T;
-  }
-
-  uint32_t hwid = 0, xcc = 0;
-  if (tid == 0) {
-    hwid = read_hw_id();
-    xcc = read_xcc_id();
   }
 
   while (valid) {
@@ -191,7 +234,7 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
         if (tid == 0 && !failed && args.claims_ahead >= 1) {
           batch_ord = next_ord;
           while (next_ord <= ord + (uint32_t)args.claims_ahead && batch_n < 2) {
-            batch[batch_n++] = claim_next(args);
+            batch[batch_n++] = claim_next(args, xcc);
             ++next_ord;
           }
         }
@@ -205,12 +248,10 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
     // per-load voffset is one of two (A) or one (B) per-lane bases plus a
     // wave-uniform step.
     constexpr uint32_t kBRowsPerLoad = 64u / CF::B_ROW_CHUNKS;  // k rows one wave-load covers
-    const uint32_t a_row0 = wave * 8u + (lane >> 3);             // row of load j = a_row0 + 32 j
-    const uint32_t a_c_even = ((lane & 7u) ^ (lane >> 3) ^ wave) & 7u;
-    const uint32_t a_c_odd = a_c_even ^ 4u;
-    const uint32_t a_base_even = a_row0 * (uint32_t)K * 2u + a_c_even * 16u;
-    const uint32_t a_base_odd = a_row0 * (uint32_t)K * 2u + a_c_odd * 16u;
-    const uint32_t b_k0 = wave * kBRowsPerLoad + lane / CF::B_ROW_CHUNKS;  // k row of load j = b_k0 + 4*kBRowsPerLoad j
+    const uint32_t a_row0 = wave * 8u + (lane >> 3);             // row of load j = a_row0 + 8 NW j
+    const uint32_t a_c0 = ((lane & 7u) ^ (lane >> 3) ^ wave) & 7u;  // chunk of load j = a_c0 ^ ((j NW) & 7)
+    const uint32_t a_base = a_row0 * (uint32_t)K * 2u;
+    const uint32_t b_k0 = wave * kBRowsPerLoad + lane / CF::B_ROW_CHUNKS;  // k row of load j = b_k0 + NW*kBRowsPerLoad j
     const uint32_t b_c = (lane % CF::B_ROW_CHUNKS) ^ swz_b(b_k0);
     const bool b_col_ok = n0 + (int32_t)(b_c * 8u) < N;
     const uint32_t b_base = b_col_ok ? (b_k0 * (uint32_t)N + b_c * 8u) * 2u : kBufOob;
@@ -226,21 +267,21 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
       const int32_t k0 = kt * CF::BK;
       const bool tail = kt >= full;
       if (j < CF::A_LOADS) {
-        const uint32_t row = a_row0 + 32u * (uint32_t)j;
-        const uint32_t c = (j & 1) ? a_c_odd : a_c_even;
-        const uint32_t vo = ((j & 1) ? a_base_odd : a_base_even) + (uint32_t)j * 64u * (uint32_t)K;
+        const uint32_t row = a_row0 + 8u * CF::NW * (uint32_t)j;
+        const uint32_t c = a_c0 ^ (uint32_t)((j * CF::NW) & 7);
+        const uint32_t vo = a_base + c * 16u + (uint32_t)j * 16u * CF::NW * (uint32_t)K;
         const bool out = (int32_t)row >= m_left || (tail && k0 + (int32_t)(c * 8u) >= K);
         return out ? kBufOob : vo;
       }
       const int jb = j - CF::A_LOADS;
-      const uint32_t krow = b_k0 + 4u * kBRowsPerLoad * (uint32_t)jb;
-      const uint32_t vo = b_base + (uint32_t)jb * 4u * kBRowsPerLoad * (uint32_t)N * 2u;
+      const uint32_t krow = b_k0 + (uint32_t)CF::NW * kBRowsPerLoad * (uint32_t)jb;
+      const uint32_t vo = b_base + (uint32_t)jb * (uint32_t)CF::NW * kBRowsPerLoad * (uint32_t)N * 2u;
       const bool out = b_base == kBufOob || (tail && k0 + (int32_t)krow >= K);
       return out ? kBufOob : vo;
     };
     auto load_dst = [&](int j) -> uint32_t {
-      return j < CF::A_LOADS ? (uint32_t)(j * 4 + (int)wave) * 1024u
-                             : (uint32_t)CF::A_STAGE + (uint32_t)((j - CF::A_LOADS) * 4 + (int)wave) * 1024u;
+      return j < CF::A_LOADS ? (uint32_t)(j * CF::NW + (int)wave) * 1024u
+                             : (uint32_t)CF::A_STAGE + (uint32_t)((j - CF::A_LOADS) * CF::NW + (int)wave) * 1024u;
     };
     // all loads of k-step kt into stage dst, back to back (prologue)
     auto issue_all = [&](int st, int32_t kt) {
@@ -405,7 +446,7 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
       if constexpr (MODE == kDynamic) {
         if (args.claims_ahead == 0 && !failed) {
           batch_ord = next_ord;
-          batch[0] = claim_next(args);
+          batch[0] = claim_next(args, xcc);
           batch_n = 1;
           ++next_ord;
         }
@@ -461,7 +502,8 @@ __global__ __launch_bounds__(256, 1) void ptg_gemm_kernel(const KernelArgs args)
 
 template <int BM, int BN, int MODE, bool GROUPED>
 static hipError_t launch_one(const KernelArgs &args, int grid, int dyn_lds, hipStream_t stream) {
-  hipLaunchKernelGGL((ptg_gemm_kernel<BM, BN, MODE, GROUPED>), dim3(grid), dim3(256), dyn_lds, stream, args);
+  hipLaunchKernelGGL((ptg_gemm_kernel<BM, BN, MODE, GROUPED>), dim3(grid), dim3(TileCfg<BM>::type::THREADS), dyn_lds,
+                     stream, args);
   return hipGetLastError();
 }
 
@@ -493,16 +535,18 @@ hipError_t launch_gemm(int tile_edge, int mode, bool grouped, const KernelArgs &
 hipError_t gemm_occupancy(int tile_edge, int dyn_lds, int *blocks_per_cu) {
   if (tile_edge == 256)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<256, 256, kDynamic, false>), 256, dyn_lds);
+        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<256, 256, kDynamic, false>),
+        TileCfg<256>::type::THREADS, dyn_lds);
   if (tile_edge == 128)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<128, 128, kDynamic, false>), 256, dyn_lds);
+        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<128, 128, kDynamic, false>),
+        TileCfg<128>::type::THREADS, dyn_lds);
   return hipErrorInvalidValue;
 }
 
 int gemm_static_lds_bytes(int tile_edge) {
-  if (tile_edge == 256) return Cfg<256, 256>::LDS + (int)sizeof(RingRec) * kRingDepth + 4;
-  if (tile_edge == 128) return Cfg<128, 128>::LDS + (int)sizeof(RingRec) * kRingDepth + 4;
+  if (tile_edge == 256) return TileCfg<256>::type::LDS + (int)sizeof(RingRec) * kRingDepth + 4;
+  if (tile_edge == 128) return TileCfg<128>::type::LDS + (int)sizeof(RingRec) * kRingDepth + 4;
   return 0;
 }
 

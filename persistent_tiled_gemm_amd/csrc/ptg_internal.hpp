@@ -17,15 +17,21 @@ struct KernelProblem {
   int32_t tile_start;  // first global tile id of this problem
 };
 
+// Tile regions of the XCD-partitioned claim policy: region x holds the tiles
+// with id mod kXcdRegions == x (MI355X has 8 XCDs; workgroup w runs on XCD w mod 8).
+static constexpr int kXcdRegions = 8;
+
 // Scheduler state in device memory. A plan keeps two sets (control block +
 // visit counters); run i uses set i % 2 and clears set (i + 1) % 2 for the next
 // run, so a run is exactly one kernel launch with no host-side reset.
 struct alignas(64) SchedCtrl {
-  uint32_t counter;    // dynamic claim counter
+  uint32_t counter;    // dynamic claim counter (single-counter policy)
   uint32_t gate;       // workgroups currently holding a concurrency slot
   uint32_t error;      // bit 0: a gate wait ran out; bit 1: ring record for the wrong ordinal
-  uint32_t pad[13];
+  uint32_t pad[5];
+  uint32_t xcd_counter[kXcdRegions];  // per-XCD claim counters (XCD-partitioned policy)
 };
+static_assert(sizeof(SchedCtrl) == 64, "control block layout");
 
 // Tile-log record as written by the kernel (tile-indexed).
 struct TileRecDev {
@@ -43,6 +49,7 @@ struct KernelArgs {
   int32_t claims_ahead;         // 0, 1 or 2 (< ring_depth)
   int32_t ring_depth;           // 2 or 3
   int32_t claim_lead;           // prefetch claims are issued this many k-steps before a tile ends
+  int32_t claim_policy;         // 0: one global counter; 1: per-XCD counters with stealing
   int32_t raster_group;         // <= 1: row-major
   uint32_t counter_base;        // added to every claim (failure forcing)
   int32_t max_concurrent;       // 0: no gate

@@ -70,7 +70,9 @@ def check_log(plan, mode, T, P=None, expected_tiles=None):
     log = ptg.gemm_read_log(plan)
     assert len(log) == T, (len(log), T)
     ran = log[log["visits"] > 0]
+    regions = 8 if int(getattr(plan.desc, "claim_policy", 0)) == 1 else 1
     errs = check_ownership(mode, T, ran["tile"], ran["worker"], ran["r0"].astype(np.float64),
-                           ran["r1"].astype(np.float64), log["visits"], P=P, expected_tiles=expected_tiles)
+                           ran["r1"].astype(np.float64), log["visits"], P=P, expected_tiles=expected_tiles,
+                           regions=regions)
     assert not errs, errs
     return log

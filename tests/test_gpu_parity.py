@@ -125,6 +125,7 @@ def test_empty_and_degenerate_inputs():
 
 def test_plan_validation():
     for bad in ({"tile_edge": 256, "claims_ahead": 3}, {"tile_edge": 256, "ring_depth": 4},
+                {"tile_edge": 256, "claim_policy": 2}, {"tile_edge": 256, "claim_lead": -1},
                 {"tile_edge": 256, "ring_depth": 2, "claims_ahead": 2}, {"tile_edge": 256, "raster": 2},
                 {"tile_edge": 256, "device": 99}):
         with pytest.raises(ptg.PtgError):
@@ -141,11 +142,12 @@ def test_plan_validation():
     plan.destroy()
 
 
+@pytest.mark.parametrize("policy", [0, 1])
 @pytest.mark.parametrize("q,depth", [(0, 3), (1, 3), (2, 3), (1, 2), (0, 2)])
-def test_claims_ahead_variants(q, depth):
+def test_claims_ahead_variants(q, depth, policy):
     p = make_problem(1280, 1024, 512, "uniform", seed=q * 10 + depth)
-    plan = make_plan(256, claims_ahead=q, ring_depth=depth)
-    say(f"case claims_ahead={q} depth={depth}")
+    plan = make_plan(256, claims_ahead=q, ring_depth=depth, claim_policy=policy)
+    say(f"case claims_ahead={q} depth={depth} policy={policy}")
     c = run(p, plan, "dynamic")
     assert_close_full(p, c)
     check_log(plan, "dynamic", 20)
@@ -194,7 +196,7 @@ def test_failure_forcing_counter_preset():
     torch = torch_mod()
     p = make_problem(2048, 512, 256, "uniform", seed=8)  # 8 x 2 tiles of 256
     T = 16
-    plan = make_plan(256)
+    plan = make_plan(256, claim_policy=0)
     for s in (0, 5, 15, 16, 40):
         say(f"case preset counter start={s}")
         A, B = upload(p)

@@ -47,3 +47,17 @@ def test_rejects_planted_errors():
     t, w, st, en, vi = _log(d, 6)
     t2 = t.copy(); t2[[1, 2]] = t2[[2, 1]]
     assert check_ownership("dynamic", 6, t2, w, st, en, vi)
+
+
+def test_region_rule_for_partitioned_claims():
+    # a worker that drains its own region (ids = 0 mod 2) and then steals from
+    # region 1 takes decreasing ids overall but increasing ids per region
+    tile = np.array([0, 2, 4, 1, 3])
+    worker = np.zeros(5, dtype=np.int64)
+    start = np.arange(5, dtype=float)
+    end = start + 1
+    visits = np.ones(5, dtype=np.int64)
+    assert check_ownership("dynamic", 5, tile, worker, start, end, visits)            # one counter: violation
+    assert not check_ownership("dynamic", 5, tile, worker, start, end, visits, regions=2)
+    bad = np.array([2, 0, 4, 1, 3])                                                    # region 0 out of order
+    assert check_ownership("dynamic", 5, bad, worker, start, end, visits, regions=2)
