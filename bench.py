@@ -235,8 +235,8 @@ def run_tail_sections(ptg, torch, stream, khz, square):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--mode", default="dynamic", choices=["nonpersistent", "static", "dynamic"])
     ap.add_argument("--claims-ahead", type=int, default=1)
     ap.add_argument("--claim-policy", type=int, default=1, choices=[0, 1],
@@ -309,6 +309,11 @@ def main():
             if mk:
                 modes[name].update(makespan_us=mk["makespan_us"], tile_median_us=mk["tile_median_us"])
         plan_other.destroy()
+        # context only: the vendor library's bf16 GEMM at the same shape (torch.matmul -> hipBLASLt). It
+        # writes a bf16 C (half of our fp32 C bytes), so it is a near, not an exact, comparison.
+        v_ms = time_runs(lambda: torch.matmul(A, B), max(5, args.steps // 2), 2, stream)
+        modes["vendor_matmul_bf16_out"] = {"ms": v_ms, "tflops": flops / (v_ms * 1e-3) / 1e12,
+                                           "frac_peak": flops / (v_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
     # sampled parity of the timed output against the oracle (a few rows)
     from oracle.gemm_ref import check_result, gemm_ref_rows, decode_bf16
