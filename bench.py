@@ -208,13 +208,14 @@ def run_tail_sections(ptg, torch, stream, khz, square):
     out["tail_boundary"] = res
     plan.destroy()
 
-    # worked example: 12 tiles of 128 x 128, at most 3 workers at once, static P = 4
+    # worked example: 12 tiles of 128 x 128, at most 3 workers at once, static P = 4; one
+    # work queue (the single claim counter), as in the example
     log("tail: worked example")
     q = make_workload("worked_example").problems[0]
     A = ptg.bf16_from_bits(q.a_bits)
     B = ptg.bf16_from_bits(q.b_bits)
     C = torch.empty((q.M, q.N), dtype=torch.float32, device="cuda")
-    plan = ptg.gemm_create(tile_edge=128, log_capacity=64, max_concurrent=3, static_workers=4,
+    plan = ptg.gemm_create(tile_edge=128, log_capacity=64, max_concurrent=3, static_workers=4, claim_policy=0,
                            min_lds_bytes=96 * 1024)
     res = {}
     for mode in modes:

@@ -79,7 +79,7 @@ struct RingRec {
 };
 
 static constexpr int kRingDepth = 3;  // LDS slots; a run uses args.ring_depth (2 or 3) of them
-static constexpr uint32_t kGateSpinLimit = 1u << 22;  // x ~1.7 us sleeps: a few seconds at most
+static constexpr uint32_t kGateSpinLimit = 1u << 22;  // polls of well under 1 us: a few seconds at most
 
 // Ask the scheduler for an alternation of one MFMA and one LDS read in the
 // current scheduling region (then the remaining MFMAs or reads).
@@ -97,24 +97,65 @@ __device__ __forceinline__ void interleave() {
 // (plus the failure-forcing base); any value >= T is a failure. XCD-partitioned
 // policy: region x (tiles 8i + x) is handed out by counter x; a worker claims
 // from its own XCD's region first (the tiles its XCD's L2 already holds
-// operands for) and, once that is exhausted, steals from the other regions in
-// turn. Each counter returns each index once, so every tile still has exactly
-// one owner; the claim fails (returns T) only when every region is exhausted.
-// A relaxed load first skips regions already seen exhausted (counters only
-// grow, so a stale value can only under-report).
-__device__ __forceinline__ uint32_t claim_next(const KernelArgs &a, uint32_t xcc) {
-  if (a.claim_policy == 0)
-    return __hip_atomic_fetch_add(&a.ctrl->counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + a.counter_base;
+// operands for) and, once that is exhausted, steals from another region. Each
+// counter returns each index once, so every tile still has exactly one owner;
+// the claim fails (returns T) only when every region is exhausted.
+//
+// A claim is split in two. claim_issue sends the first atomic (the global
+// counter, or the counter of the worker's current region: its own XCD's to
+// begin with) from lane 0 and returns its raw answer in lane 0's register
+// without waiting for it, so the round trip hides under the MFMAs of the
+// current tile. claim_resolve, called by a whole wave (all lanes active) once
+// the answer is needed, broadcasts it and turns it into a tile id: every
+// decision is wave-uniform and the scheduler state lives in scalar registers.
+// Only when the current region is exhausted does it steal: it reads all eight
+// counters at once (lanes 0-7), picks the first region after the worker's own
+// that still has work, claims from it and makes it the current region, so the
+// following claims are again a single hidden atomic. A claim that comes back
+// out of range proves that region exhausted for good (counters only grow), so
+// at most eight steal attempts are made.
+__device__ __forceinline__ uint32_t lane0_fetch_add(uint32_t *ctr, uint32_t lane) {
+  uint32_t v = 0;
+  if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ uint32_t region_size(uint32_t T, uint32_t y) {
+  return T > y ? (T - y + kXcdRegions - 1) / kXcdRegions : 0u;
+}
+__device__ __forceinline__ uint32_t claim_issue(const KernelArgs &a, uint32_t region, uint32_t lane) {
+  uint32_t *ctr = a.claim_policy == 0 ? &a.ctrl->counter : &a.ctrl->xcd_counter[region];
+  uint32_t v = 0;
+  if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+__device__ __forceinline__ uint32_t claim_resolve(const KernelArgs &a, uint32_t xcc, uint32_t lane, uint32_t raw,
+                                                  uint32_t &region) {
+  const uint32_t i0 = __builtin_amdgcn_readfirstlane(raw);
+  if (a.claim_policy == 0) return i0 + a.counter_base;
   const uint32_t T = (uint32_t)a.T;
-  for (uint32_t r = 0; r < (uint32_t)kXcdRegions; ++r) {
+  if (i0 < region_size(T, region)) return i0 * (uint32_t)kXcdRegions + region;
+  // lane r < 8 watches region (xcc + r) mod 8
+  const uint32_t my_y = (xcc + (lane & 7u)) % (uint32_t)kXcdRegions;
+  for (int attempt = 0; attempt < kXcdRegions; ++attempt) {
+    bool open = false;
+    if (lane < (uint32_t)kXcdRegions) {
+      const uint32_t seen = __hip_atomic_load(&a.ctrl->xcd_counter[my_y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      open = seen < region_size(T, my_y);
+    }
+    const uint64_t mask = __ballot(open);
+    if (mask == 0) return T;
+    const uint32_t r = (uint32_t)__builtin_ctzll(mask);
     const uint32_t y = (xcc + r) % (uint32_t)kXcdRegions;
-    const uint32_t size = T > y ? (T - y + kXcdRegions - 1) / kXcdRegions : 0u;
-    uint32_t *ctr = &a.ctrl->xcd_counter[y];
-    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= size) continue;
-    const uint32_t i = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (i < size) return i * (uint32_t)kXcdRegions + y;
+    const uint32_t i = lane0_fetch_add(&a.ctrl->xcd_counter[y], lane);
+    if (i < region_size(T, y)) {
+      region = y;
+      return i * (uint32_t)kXcdRegions + y;
+    }
   }
   return T;
+}
+__device__ __forceinline__ uint32_t claim_next(const KernelArgs &a, uint32_t xcc, uint32_t lane, uint32_t &region) {
+  return claim_resolve(a, xcc, lane, claim_issue(a, region, lane), region);
 }
 
 template <int BM, int BN, int MODE, bool GROUPED>
@@ -158,7 +199,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
           ok = 1;
           break;
         }
-        __builtin_amdgcn_s_sleep(64);
+        __builtin_amdgcn_s_sleep(4);
       }
       if (!ok) __hip_atomic_fetch_or(&args.ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       gate_ok = ok;
@@ -167,23 +208,23 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     if (!gate_ok) return;
   }
 
-  uint32_t hwid = 0, xcc = 0;
-  if (tid == 0) {
-    hwid = read_hw_id();
-    xcc = read_xcc_id() % (uint32_t)kXcdRegions;
-  }
+  // scalar reads, kept per wave (only wave 0's values are logged and used to claim)
+  const uint32_t hwid = read_hw_id();
+  const uint32_t xcc = read_xcc_id() % (uint32_t)kXcdRegions;
 
   // ---- first tile
   uint32_t ord = 0;       // this worker's tile ordinal
   uint32_t tile = 0;
   bool valid = false;
-  uint32_t next_ord = 1;  // producer: next ordinal to claim
-  bool failed = false;    // producer: a claim has come back invalid
+  // producer state (wave 0, the elected producer, holds the meaningful copy)
+  uint32_t next_ord = 1;  // next ordinal to claim
+  bool failed = false;    // a claim has come back invalid
+  uint32_t region = xcc;  // region the next claim is sent to (XCD-partitioned policy)
   if constexpr (MODE == kDynamic) {
-    if (tid == 0) {
-      const uint32_t v = claim_next(args, xcc);
+    if (wave == 0) {
+      const uint32_t v = claim_next(args, xcc, lane, region);
       const uint32_t ok = v < (uint32_t)T ? 1u : 0u;
-      ring[0] = RingRec{v, ok, 0u, 0u};
+      if (lane == 0) ring[0] = RingRec{v, ok, 0u, 0u};
       failed = !ok;
     }
     __syncthreads();
@@ -220,21 +261,20 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     const int32_t m0 = m_t * BM, n0 = n_t * BN;
     const int32_t M = pb.M, N = pb.N, K = pb.K;
 
-    uint64_t t0 = 0, r0 = 0;
-    if (tid == 0) {
-      t0 = clock_core();
-      r0 = clock_wall();
-    }
+    const uint64_t t0 = clock_core();
+    const uint64_t r0 = clock_wall();
 
     // ---- claim ahead (the throttle: at most claims_ahead beyond the current tile)
-    uint32_t batch[2] = {0u, 0u};
+    uint32_t batch[2] = {0u, 0u};  // raw answers of the claims issued during this tile (lane 0)
     uint32_t batch_ord = 0, batch_n = 0;
     auto do_claims = [&]() {
       if constexpr (MODE == kDynamic) {
-        if (tid == 0 && !failed && args.claims_ahead >= 1) {
+        if (wave == 0 && !failed && args.claims_ahead >= 1) {
           batch_ord = next_ord;
           while (next_ord <= ord + (uint32_t)args.claims_ahead && batch_n < 2) {
-            batch[batch_n++] = claim_next(args, xcc);
+            const uint32_t v = claim_issue(args, region, lane);
+            if (batch_n == 0) batch[0] = v; else batch[1] = v;
+            ++batch_n;
             ++next_ord;
           }
         }
@@ -442,21 +482,23 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     }
 
     // ---- publish the next claim (producer) and log the tile
-    if (tid == 0) {
+    if (wave == 0) {
       if constexpr (MODE == kDynamic) {
         if (args.claims_ahead == 0 && !failed) {
           batch_ord = next_ord;
-          batch[0] = claim_next(args, xcc);
+          batch[0] = claim_issue(args, region, lane);
           batch_n = 1;
           ++next_ord;
         }
         for (uint32_t b = 0; b < batch_n; ++b) {
-          const uint32_t v = batch[b];
+          const uint32_t v = claim_resolve(args, xcc, lane, b == 0 ? batch[0] : batch[1], region);
           const uint32_t ok = v < (uint32_t)T ? 1u : 0u;
           if (!ok) failed = true;
-          ring[(batch_ord + b) % (uint32_t)args.ring_depth] = RingRec{v, ok, batch_ord + b, 0u};
+          if (lane == 0) ring[(batch_ord + b) % (uint32_t)args.ring_depth] = RingRec{v, ok, batch_ord + b, 0u};
         }
       }
+    }
+    if (tid == 0) {
       const uint64_t t1 = clock_core();
       const uint64_t r1 = clock_wall();
       if ((int32_t)tile < args.log_cap) {

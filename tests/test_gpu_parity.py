@@ -219,3 +219,19 @@ def test_failure_forcing_counter_preset():
     assert_close_full(p, c)
     check_log(plan, "dynamic", T)
     plan.destroy()
+
+
+@pytest.mark.parametrize("shape,cap", [((1280, 1024, 128), 1), ((768, 768, 64), 2), ((256, 512, 64), 1)])
+def test_xcd_regions_drained_by_stealing(shape, cap):
+    # with at most `cap` workers alive, the few workers must drain every XCD region,
+    # most of them by stealing; T = 20, 9 and 2 leave some regions empty or uneven
+    M, N, K = shape
+    p = make_problem(M, N, K, "uniform", seed=M + cap)
+    plan = make_plan(256, claim_policy=1, max_concurrent=cap, min_lds_bytes=96 * 1024)
+    T = -(-M // 256) * -(-N // 256)
+    say(f"case xcd stealing shape={shape} cap={cap} T={T}")
+    c = run(p, plan, "dynamic")
+    assert_close_full(p, c)
+    log = check_log(plan, "dynamic", T)
+    assert len(np.unique(log["worker"])) <= T
+    plan.destroy()

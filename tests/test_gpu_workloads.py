@@ -154,12 +154,14 @@ def test_partial_occupancy_co_run(square):
 def test_worked_example_concurrency_cap():
     """12 tiles of 128 x 128, at most 3 workers at once, static P = 4: the log shows
     at most 3 tiles in flight at any moment and the static makespan exceeds the
-    dynamic one (the pages' 6t vs 4t; the exact ratio is a hardware fact)."""
+    dynamic one (the pages' 6t vs 4t; the exact ratio is a hardware fact). The example
+    has one work queue, so the dynamic mode uses the single claim counter: with 12
+    tiles over 8 XCD regions almost every claim would be a steal."""
     torch = torch_mod()
     p = make_workload("worked_example").problems[0]
     A, B = ptg.bf16_from_bits(p.a_bits), ptg.bf16_from_bits(p.b_bits)
     C = torch.empty((p.M, p.N), dtype=torch.float32, device="cuda")
-    plan = ptg.gemm_create(tile_edge=128, log_capacity=64, max_concurrent=3, static_workers=4,
+    plan = ptg.gemm_create(tile_edge=128, log_capacity=64, max_concurrent=3, static_workers=4, claim_policy=0,
                            min_lds_bytes=96 * 1024)
     spans = {}
     for mode in MODES:
