@@ -23,6 +23,18 @@
  *                             blog post (sections "cancelling the launch ..." and
  *                             "following the CUTLASS source"), which gfx950 lacks.
  *
+ * Tail splitting (optional, tail_split >= 2; single GEMMs only). Whole tiles
+ * quantise the finish: T = P + 1 tiles on P workers take two tile times. The
+ * blog post names splitting work along K as what removes this and leaves it out
+ * of its design (first section); here it is the work-unit decomposition of a
+ * run: the tiles that fill whole waves of workers stay whole units, and each
+ * of the r = T mod P tiles of the partial last wave becomes S units, K-chunks
+ * of nearly equal k-step counts. Every unit still has exactly one owner under
+ * every scheduler. A chunk writes its fp32 partial tile to plan scratch; the
+ * workgroup that completes a tile's last chunk adds the S partials in chunk
+ * order (a fixed order: results do not depend on which chunk finished last)
+ * and writes C. Split tiles therefore round differently from whole tiles.
+ *
  * Layouts. Row-major and contiguous: A is M x K (lda = K), B is K x N (ldb = N),
  * C is M x N (ldc = N). bf16 is passed as raw 16-bit patterns. Device pointers
  * only (hipMalloc / torch device memory). A, B and C must be 16-byte aligned;
@@ -74,6 +86,7 @@ typedef enum gemm_sched_mode {
 #define GEMM_MAX_N (1 << 22)
 #define GEMM_MAX_M (1 << 30)
 #define GEMM_MAX_TILES (1 << 30)
+#define GEMM_MAX_TAIL_SPLIT 64
 
 /*
  * Plan descriptor (a value type; gemm_create copies it). Fields:
@@ -99,12 +112,18 @@ typedef enum gemm_sched_mode {
  *   raster          0 = row-major tile order; 1 = grouped-M with group height
  *                   raster_group tile rows.
  *   static_workers  static mode's P; 0 = resident workgroups (occupancy x CUs).
- *   log_capacity    tiles to log per run; 0 turns the tile log off.
+ *   log_capacity    work units to log per run; 0 turns the log off.
  *   min_lds_bytes   dynamic LDS padding per workgroup (limits residency; 0 = none).
  *   max_concurrent  0 = no cap; n > 0 lets at most n workgroups compute at once
  *                   (a device-side gate with a bounded wait).
  *   max_groups      capacity of the grouped-problem table (0 = 1024).
  *   device          HIP device ordinal; must be gfx950.
+ *   tail_split      0 = off. s in 2..GEMM_MAX_TAIL_SPLIT: split each tile of a
+ *                   partial last wave into at most s K-chunks (fewer when the
+ *                   idle workers or K, at >= 4 k-steps a chunk, allow fewer).
+ *                   Workers per wave: the static mode's P, else occupancy x
+ *                   CUs. gemm_create then reserves the partial-sum scratch:
+ *                   bm x bn x 4 bytes per worker of one wave.
  */
 typedef struct gemm_tile_desc {
   int32_t bm, bn, bk;
@@ -120,24 +139,30 @@ typedef struct gemm_tile_desc {
   int32_t max_concurrent;
   int32_t max_groups;
   int32_t device;
+  int32_t tail_split;
 } gemm_tile_desc;
 
 /* Opaque plan: the tile_cfg argument of gemm_run. Owns all library scratch. */
 typedef struct gemm_plan *gemm_tile_cfg;
 
 /*
- * One tile-log record (host copy). tile: tile id in raster order (grouped: ids
- * of problem g follow those of problems < g); worker: launch slot (blockIdx.x)
- * that ran it; hw_id / xcc_id: raw HW_ID and XCC_ID hardware registers of the
- * wave that ran it; t0/t1: s_memtime at tile start / after its stores were
- * issued; r0/r1: the same moments on the constant-rate s_memrealtime clock
- * (rate: gemm_plan_info's wallclock_khz); visits: how many times the tile was
- * finished (exactly-once => 1); problem: grouped problem index (0 otherwise).
+ * One work-unit log record (host copy), indexed by unit id. Without tail
+ * splitting units are tiles (unit == tile). unit: the work-unit id the
+ * schedulers hand out; tile: output tile id in raster order (grouped: ids of
+ * problem g follow those of problems < g); k_begin/k_end: the K range [k_begin,
+ * k_end) the unit accumulated (the whole K for a whole tile); worker: launch
+ * slot (blockIdx.x) that ran it; hw_id / xcc_id: raw HW_ID and XCC_ID hardware
+ * registers of the wave that ran it; t0/t1: s_memtime at unit start / after
+ * its stores were issued; r0/r1: the same moments on the constant-rate
+ * s_memrealtime clock (rate: gemm_plan_info's wallclock_khz); visits: how many
+ * times the unit was finished (exactly-once => 1); problem: grouped problem
+ * index (0 otherwise).
  */
 typedef struct gemm_tile_rec {
   uint32_t tile, worker, hw_id, xcc_id;
   uint64_t t0, t1, r0, r1;
   uint32_t visits, problem;
+  uint32_t unit, k_begin, k_end, pad;
 } gemm_tile_rec;
 
 /* Facts about a plan and its last run. */
@@ -148,6 +173,9 @@ typedef struct gemm_plan_info {
   int32_t static_workers;    /* P the static mode uses for a large problem */
   int64_t wallclock_khz;     /* s_memrealtime rate */
   int64_t last_tiles;        /* T of the last run */
+  int64_t last_units;        /* work units of the last run (== last_tiles unless split) */
+  int64_t last_split_base;   /* first split tile (== last_tiles when nothing was split) */
+  int32_t last_split_chunks; /* K-chunks per split tile (1 when nothing was split) */
   int64_t last_grid;         /* grid size of the last run */
   int32_t last_mode;         /* scheduler of the last run (-1 before the first) */
   int32_t lds_bytes;         /* LDS per workgroup */
@@ -178,8 +206,10 @@ gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const 
                              int32_t sched_mode, gemm_tile_cfg tile_cfg, void *stream);
 
 /*
- * Synchronise the last run's stream and copy its tile log to host_out (up to
- * cap records, in tile-id order, including tiles that never ran: visits == 0).
+ * Synchronise the last run's stream and copy its log to host_out (up to cap
+ * records, in unit-id order, including units that never ran: visits == 0; for
+ * those, tile and k_begin/k_end are what the launch planned and worker is
+ * 0xFFFFFFFF).
  * *n_out receives the number of records written. Returns GEMM_E_TIMEOUT if a
  * workgroup of the run gave up waiting at the concurrency gate, GEMM_E_SCHED if
  * a consumer found a ring record for the wrong ordinal (the log is still copied).

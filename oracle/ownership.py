@@ -24,6 +24,13 @@ any worker finished that tile. The rules:
 
 Timestamps are taken on the GPU's constant-rate clock; makespan = latest tile
 end - earliest tile start over the tiles that ran.
+
+Split tails. When the tiles of a partial last wave are split along K (the
+remedy for whole-tile quantisation that [CLC]'s first section names and leaves
+out), the unit of ownership becomes the work unit: a whole tile, or one K-chunk
+of a split tile. The rules above then hold for unit ids, and in addition the K
+ranges of each tile's units must partition [0, K) exactly (check_k_cover):
+every product a[m][k] b[k][n] enters C once.
 """
 
 from __future__ import annotations
@@ -32,7 +39,7 @@ from typing import Dict, Iterable, List, Optional
 
 import numpy as np
 
-__all__ = ["check_ownership", "makespan", "per_worker"]
+__all__ = ["check_ownership", "check_k_cover", "split_units", "makespan", "per_worker"]
 
 
 def per_worker(worker: np.ndarray, tiles: np.ndarray) -> Dict[int, np.ndarray]:
@@ -115,3 +122,66 @@ def check_ownership(mode: str, T: int, tile: np.ndarray, worker: np.ndarray, sta
     elif mode != "dynamic":
         errs.append(f"unknown mode {mode}")
     return errs
+
+
+def check_k_cover(tile: np.ndarray, k_begin: np.ndarray, k_end: np.ndarray, T: int, K) -> List[str]:
+    """Violations of "the units of each tile cover its K range exactly once".
+
+    ``tile``, ``k_begin``, ``k_end`` are per-unit arrays (units that ran); ``K`` is
+    the reduction length, one int for all tiles or an array of length T.
+    """
+    errs: List[str] = []
+    tile = np.asarray(tile, dtype=np.int64)
+    kb = np.asarray(k_begin, dtype=np.int64)
+    ke = np.asarray(k_end, dtype=np.int64)
+    Ks = np.broadcast_to(np.asarray(K, dtype=np.int64), (T,))
+    if np.any(ke < kb):
+        errs.append("a unit ends its K range before it starts")
+    spans: Dict[int, List[tuple]] = {}
+    for t, b, e in zip(tile.tolist(), kb.tolist(), ke.tolist()):
+        if not 0 <= t < T:
+            errs.append(f"unit for tile {t} outside 0..{T - 1}")
+            continue
+        spans.setdefault(int(t), []).append((int(b), int(e)))
+    for t in range(T):
+        iv = sorted(spans.get(t, []))
+        if not iv:
+            errs.append(f"tile {t} has no unit")
+            continue
+        pos = 0
+        for b, e in iv:
+            if b != pos:
+                errs.append(f"tile {t}: K range {'gap' if b > pos else 'overlap'} at {min(b, pos)}")
+                break
+            pos = e
+        else:
+            if pos != int(Ks[t]):
+                errs.append(f"tile {t}: K covered up to {pos}, not {int(Ks[t])}")
+    return errs
+
+
+def split_units(T: int, workers: int, nk: int, max_chunks: int, min_chunk_steps: int = 4,
+                max_split_tiles: int = 1024):
+    """The work units of one run as (tile, first k-step, end k-step) triples, unit-id order.
+
+    Tiles that fill whole waves of ``workers`` stay whole; each of the
+    r = T mod workers tiles of the partial last wave is cut into
+    S = min(max_chunks, workers // r, nk // min_chunk_steps) K-chunks when S >= 2,
+    chunk c covering k-steps [floor(c nk / S), floor((c+1) nk / S)). Units of the
+    split tiles follow the whole ones, tile-major.
+    """
+    whole = [(t, 0, nk) for t in range(T)]
+    if max_chunks < 2 or workers < 2 or T < workers:
+        return whole
+    r = T % workers
+    if r == 0 or r > max_split_tiles:
+        return whole
+    S = min(max_chunks, workers // r, nk // min_chunk_steps)
+    if S < 2:
+        return whole
+    base = T - r
+    units = [(t, 0, nk) for t in range(base)]
+    for q in range(r):
+        for c in range(S):
+            units.append((base + q, (c * nk) // S, ((c + 1) * nk) // S))
+    return units

@@ -51,27 +51,30 @@ class PtgError(RuntimeError):
 class TileDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bm", "bn", "bk", "ring_depth", "claims_ahead", "claim_lead", "claim_policy", "raster", "raster_group", "static_workers",
-        "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device")]
+        "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device", "tail_split")]
 
 
 class TileRec(ctypes.Structure):
     _fields_ = [("tile", ctypes.c_uint32), ("worker", ctypes.c_uint32), ("hw_id", ctypes.c_uint32),
                 ("xcc_id", ctypes.c_uint32), ("t0", ctypes.c_uint64), ("t1", ctypes.c_uint64),
                 ("r0", ctypes.c_uint64), ("r1", ctypes.c_uint64), ("visits", ctypes.c_uint32),
-                ("problem", ctypes.c_uint32)]
+                ("problem", ctypes.c_uint32), ("unit", ctypes.c_uint32), ("k_begin", ctypes.c_uint32),
+                ("k_end", ctypes.c_uint32), ("pad", ctypes.c_uint32)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("device", ctypes.c_int32), ("cu_count", ctypes.c_int32), ("occupancy", ctypes.c_int32),
                 ("static_workers", ctypes.c_int32), ("wallclock_khz", ctypes.c_int64),
-                ("last_tiles", ctypes.c_int64), ("last_grid", ctypes.c_int64), ("last_mode", ctypes.c_int32),
+                ("last_tiles", ctypes.c_int64), ("last_units", ctypes.c_int64), ("last_split_base", ctypes.c_int64),
+                ("last_split_chunks", ctypes.c_int32), ("last_grid", ctypes.c_int64), ("last_mode", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32)]
 
 
 TILE_REC_DTYPE = np.dtype([("tile", "<u4"), ("worker", "<u4"), ("hw_id", "<u4"), ("xcc_id", "<u4"),
                            ("t0", "<u8"), ("t1", "<u8"), ("r0", "<u8"), ("r1", "<u8"),
-                           ("visits", "<u4"), ("problem", "<u4")])
-assert TILE_REC_DTYPE.itemsize == ctypes.sizeof(TileRec) == 56
+                           ("visits", "<u4"), ("problem", "<u4"), ("unit", "<u4"), ("k_begin", "<u4"),
+                           ("k_end", "<u4"), ("pad", "<u4")])
+assert TILE_REC_DTYPE.itemsize == ctypes.sizeof(TileRec) == 72
 
 _lib = None
 

@@ -28,8 +28,11 @@ struct gemm_plan {
   int64_t wallclock_khz = 0;
   int lds_bytes = 0;
   int dyn_lds = 0;
-  // device scratch: two sets of [SchedCtrl][visits u32 x log_capacity], plus the log
+  // device scratch: two sets of [SchedCtrl][arrivals u32 x kMaxSplitTiles][visits u32 x
+  // log_capacity], plus the log and (tail splitting on) the partial-sum workspace
   unsigned char *d_ctrl_block = nullptr;
+  float *d_ws = nullptr;
+  int64_t ws_tiles = 0;  // BM x BN fp32 partial slots in d_ws
   size_t ctrl_set_bytes = 0;
   uint64_t runs = 0;  // launches so far; run i uses set i % 2
   TileRecDev *d_log = nullptr;
@@ -44,9 +47,13 @@ struct gemm_plan {
   hipStream_t last_stream = nullptr;
   bool has_run = false;
   int64_t last_tiles = 0;
+  int64_t last_units = 0;
+  int64_t last_split_base = 0;
+  int32_t last_split_chunks = 0;
   int64_t last_grid = 0;
   int32_t last_mode = -1;
   std::vector<int32_t> last_tile_start;  // per problem (grouped), for log decoding
+  std::vector<int32_t> last_k;           // K per problem, for log decoding
   std::string last_error;
 };
 
@@ -86,12 +93,48 @@ gemm_status check_current_device(gemm_plan *p) {
 }
 
 unsigned char *ctrl_set(gemm_plan *p, uint64_t run) { return p->d_ctrl_block + (run & 1u) * p->ctrl_set_bytes; }
+constexpr size_t kArrivalsOffset = sizeof(SchedCtrl);
+constexpr size_t kVisitsOffset = sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)ptg::kMaxSplitTiles;
 
-gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, int64_t tiles, hipStream_t s) {
+// Fewest k-steps a K-chunk of a split tile gets.
+constexpr int64_t kMinChunkSteps = 4;
+
+// Work units of a run: T whole tiles, or, with tail splitting on, the tiles
+// that fill whole waves of `workers` plus the r = T mod workers tiles of the
+// partial last wave, each split into S K-chunks (S <= tail_split, <= workers / r
+// so the chunks fit the idle workers, and >= kMinChunkSteps k-steps each).
+void plan_units(const gemm_plan *p, bool grouped, int32_t mode, int64_t tiles, int64_t K, int64_t *units,
+                int64_t *split_base, int32_t *chunks) {
+  *units = tiles;
+  *split_base = tiles;
+  *chunks = 1;
+  if (grouped || p->desc.tail_split < 2 || p->ws_tiles == 0) return;
+  const int64_t workers =
+      mode == GEMM_SCHED_STATIC ? (int64_t)p->static_workers : (int64_t)p->occupancy * p->cu_count;
+  if (workers < 2 || tiles < workers) return;
+  const int64_t r = tiles % workers;
+  if (r == 0 || r > ptg::kMaxSplitTiles) return;
+  const int64_t nk = ceil_div(K, p->desc.bk);
+  const int64_t S = std::min<int64_t>({(int64_t)p->desc.tail_split, workers / r, nk / kMinChunkSteps, p->ws_tiles / r});
+  if (S < 2) return;
+  *split_base = tiles - r;
+  *chunks = (int32_t)S;
+  *units = tiles - r + r * S;
+}
+
+gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, int64_t tiles, int64_t K,
+                   hipStream_t s) {
   if (mode < GEMM_SCHED_NONPERSISTENT || mode > GEMM_SCHED_DYNAMIC) return GEMM_E_INVALID_ARG;
-  int64_t grid = tiles;
-  if (mode == GEMM_SCHED_STATIC) grid = std::min<int64_t>(tiles, p->static_workers);
-  args.T = (int32_t)tiles;
+  int64_t units = tiles, split_base = tiles;
+  int32_t chunks = 1;
+  plan_units(p, grouped, mode, tiles, K, &units, &split_base, &chunks);
+  if (units > GEMM_MAX_TILES) return GEMM_E_SHAPE;
+  int64_t grid = units;
+  if (mode == GEMM_SCHED_STATIC) grid = std::min<int64_t>(units, p->static_workers);
+  args.T = (int32_t)units;
+  args.split_base = (int32_t)split_base;
+  args.split_chunks = chunks;
+  args.ws = p->d_ws;
   args.P = (int32_t)grid;
   args.claims_ahead = p->desc.claims_ahead;
   args.ring_depth = p->desc.ring_depth;
@@ -107,10 +150,11 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   args.log_cap = p->desc.log_capacity;
   unsigned char *cur = ctrl_set(p, p->runs), *nxt = ctrl_set(p, p->runs + 1);
   args.ctrl = reinterpret_cast<SchedCtrl *>(cur);
-  args.visits = reinterpret_cast<uint32_t *>(cur + sizeof(SchedCtrl));
+  args.arrivals = reinterpret_cast<uint32_t *>(cur + kArrivalsOffset);
+  args.visits = reinterpret_cast<uint32_t *>(cur + kVisitsOffset);
   args.ctrl_next = reinterpret_cast<SchedCtrl *>(nxt);
-  args.visits_next = reinterpret_cast<uint32_t *>(nxt + sizeof(SchedCtrl));
-  args.clear_count = p->desc.log_capacity;
+  args.clear_next = reinterpret_cast<uint32_t *>(nxt + kArrivalsOffset);
+  args.clear_count = ptg::kMaxSplitTiles + p->desc.log_capacity;
   args.log = p->d_log;
   hipError_t e = ptg::launch_gemm(p->desc.bm, mode, grouped, args, (int)grid, p->dyn_lds, s);
   if (e != hipSuccess) return hip_fail(p, e, "kernel launch");
@@ -118,6 +162,9 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   p->last_stream = s;
   p->has_run = true;
   p->last_tiles = tiles;
+  p->last_units = units;
+  p->last_split_base = split_base;
+  p->last_split_chunks = chunks;
   p->last_grid = grid;
   p->last_mode = mode;
   return GEMM_OK;
@@ -160,6 +207,7 @@ gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t de
   out->max_concurrent = 0;
   out->max_groups = 1024;
   out->device = device;
+  out->tail_split = 0;
   return GEMM_OK;
 }
 
@@ -173,7 +221,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (d.claim_lead < 0 || d.claim_policy < 0 || d.claim_policy > 1) return GEMM_E_INVALID_ARG;
   if (d.raster < 0 || d.raster > 1 || (d.raster == 1 && d.raster_group < 1)) return GEMM_E_INVALID_ARG;
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
-      d.max_groups < 0)
+      d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT)
     return GEMM_E_INVALID_ARG;
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -212,7 +260,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   p->occupancy = occ;
   p->static_workers = d.static_workers > 0 ? d.static_workers : occ * p->cu_count;
 
-  p->ctrl_set_bytes = (sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)std::max(d.log_capacity, 1) + 255) & ~(size_t)255;
+  p->ctrl_set_bytes = (kVisitsOffset + sizeof(uint32_t) * (size_t)std::max(d.log_capacity, 1) + 255) & ~(size_t)255;
   if (hipMalloc(&p->d_ctrl_block, 2 * p->ctrl_set_bytes) != hipSuccess) {
     delete p;
     return GEMM_E_NOMEM;
@@ -223,6 +271,16 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   }
   if (d.log_capacity > 0) {
     if (hipMalloc(&p->d_log, sizeof(TileRecDev) * (size_t)d.log_capacity) != hipSuccess) {
+      gemm_destroy(p);
+      return GEMM_E_NOMEM;
+    }
+  }
+  if (d.tail_split >= 2) {
+    // the K-chunks of one run never outnumber the workers of one wave
+    p->ws_tiles = std::max<int64_t>((int64_t)occ * p->cu_count, p->static_workers);
+    if (hipMalloc(&p->d_ws, sizeof(float) * (size_t)d.bm * (size_t)d.bn * (size_t)p->ws_tiles) != hipSuccess) {
+      p->d_ws = nullptr;
+      p->ws_tiles = 0;
       gemm_destroy(p);
       return GEMM_E_NOMEM;
     }
@@ -273,7 +331,8 @@ gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t 
   args.groups = nullptr;
   args.G = 1;
   p->last_tile_start.assign(1, 0);
-  return launch(p, sched_mode, false, args, tiles, static_cast<hipStream_t>(stream));
+  p->last_k.assign(1, (int32_t)K);
+  return launch(p, sched_mode, false, args, tiles, K, static_cast<hipStream_t>(stream));
 }
 
 gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const *B, float *const *C,
@@ -285,7 +344,7 @@ gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const 
   if (G > p->desc.max_groups) return GEMM_E_SHAPE;
   if (sched_mode < GEMM_SCHED_NONPERSISTENT || sched_mode > GEMM_SCHED_DYNAMIC) return GEMM_E_INVALID_ARG;
   std::vector<KernelProblem> probs((size_t)G);
-  std::vector<int32_t> starts((size_t)G);
+  std::vector<int32_t> starts((size_t)G), ks((size_t)G);
   int64_t tiles = 0;
   for (int32_t g = 0; g < G; ++g) {
     gemm_status st = check_problem(A[g], B[g], C[g], M[g], N[g], K[g]);
@@ -301,6 +360,7 @@ gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const 
     q.tiles_n = (int32_t)ceil_div(N[g], p->desc.bn);
     q.tile_start = (int32_t)tiles;
     starts[(size_t)g] = (int32_t)tiles;
+    ks[(size_t)g] = (int32_t)K[g];
     tiles += (int64_t)q.tiles_m * q.tiles_n;
     if (tiles > GEMM_MAX_TILES) return GEMM_E_SHAPE;
   }
@@ -331,7 +391,8 @@ gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const 
   args.groups = p->d_groups;
   args.G = G;
   p->last_tile_start = starts;
-  return launch(p, sched_mode, true, args, tiles, s);
+  p->last_k = ks;
+  return launch(p, sched_mode, true, args, tiles, 0, s);
 }
 
 gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_t cap, size_t *n_out) {
@@ -341,7 +402,7 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
   if (!p->has_run || p->desc.log_capacity == 0) return GEMM_OK;
   hipError_t e = hipStreamSynchronize(p->last_stream);
   if (e != hipSuccess) return hip_fail(p, e, "hipStreamSynchronize");
-  const size_t n = (size_t)std::min<int64_t>(p->last_tiles, p->desc.log_capacity);
+  const size_t n = (size_t)std::min<int64_t>(p->last_units, p->desc.log_capacity);
   const size_t m = std::min(n, cap);
   std::vector<TileRecDev> recs(m);
   std::vector<uint32_t> visits(m);
@@ -349,21 +410,42 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
   if (m > 0) {
     e = hipMemcpy(recs.data(), p->d_log, sizeof(TileRecDev) * m, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(log)");
-    e = hipMemcpy(visits.data(), ctrl_set(p, p->runs - 1) + sizeof(SchedCtrl), sizeof(uint32_t) * m,
+    e = hipMemcpy(visits.data(), ctrl_set(p, p->runs - 1) + kVisitsOffset, sizeof(uint32_t) * m,
                   hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(visits)");
   }
   e = hipMemcpy(&ctrl, ctrl_set(p, p->runs - 1), sizeof(ctrl), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(ctrl)");
+  const int64_t bk = p->desc.bk;
   for (size_t i = 0; i < m; ++i) {
     gemm_tile_rec &r = host_out[i];
     std::memset(&r, 0, sizeof(r));
     r.visits = visits[i];
+    r.unit = (uint32_t)i;
+    // the unit's tile and K range as the launch planned them
+    int64_t tile = (int64_t)i, chunk = 0;
+    const int64_t S = p->last_split_chunks;
+    if ((int64_t)i >= p->last_split_base) {
+      tile = p->last_split_base + ((int64_t)i - p->last_split_base) / S;
+      chunk = ((int64_t)i - p->last_split_base) % S;
+    }
+    const auto &ts = p->last_tile_start;
+    const size_t g = (size_t)(std::upper_bound(ts.begin(), ts.end(), (int32_t)tile) - ts.begin() - 1);
+    const int64_t Kg = p->last_k.empty() ? 0 : p->last_k[g];
+    const int64_t nk = ceil_div(Kg, bk);
+    const int64_t kb = (int64_t)i >= p->last_split_base ? nk * chunk / S : 0;
+    const int64_t ke = (int64_t)i >= p->last_split_base ? nk * (chunk + 1) / S : nk;
+    r.problem = (uint32_t)g;
     if (visits[i] == 0) {
-      r.tile = (uint32_t)i;
+      r.tile = (uint32_t)tile;
+      r.k_begin = (uint32_t)std::min(kb * bk, Kg);
+      r.k_end = (uint32_t)std::min(ke * bk, Kg);
       r.worker = 0xFFFFFFFFu;
       continue;
     }
+    // what the kernel recorded (the tests compare it with the plan above)
+    r.k_begin = (uint32_t)std::min((int64_t)recs[i].kb * bk, Kg);
+    r.k_end = (uint32_t)std::min((int64_t)recs[i].ke * bk, Kg);
     r.tile = recs[i].tile;
     r.worker = recs[i].worker;
     r.hw_id = recs[i].hw_id;
@@ -372,9 +454,6 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
     r.t1 = recs[i].t1;
     r.r0 = recs[i].r0;
     r.r1 = recs[i].r1;
-    const auto &ts = p->last_tile_start;
-    const auto it = std::upper_bound(ts.begin(), ts.end(), (int32_t)i);
-    r.problem = (uint32_t)(it - ts.begin() - 1);
   }
   *n_out = m;
   if (ctrl.error != 0) {
@@ -394,6 +473,9 @@ gemm_status gemm_plan_info_get(gemm_tile_cfg tile_cfg, gemm_plan_info *out) {
   out->static_workers = p->static_workers;
   out->wallclock_khz = p->wallclock_khz;
   out->last_tiles = p->last_tiles;
+  out->last_units = p->last_units;
+  out->last_split_base = p->last_split_base;
+  out->last_split_chunks = p->last_split_chunks;
   out->last_grid = p->last_grid;
   out->last_mode = p->last_mode;
   out->lds_bytes = p->lds_bytes;
@@ -407,6 +489,7 @@ gemm_status gemm_destroy(gemm_tile_cfg tile_cfg) {
   if (p->groups_event_pending && p->groups_uploaded) (void)hipEventSynchronize(p->groups_uploaded);
   if (p->d_ctrl_block) (void)hipFree(p->d_ctrl_block);
   if (p->d_log) (void)hipFree(p->d_log);
+  if (p->d_ws) (void)hipFree(p->d_ws);
   if (p->d_groups) (void)hipFree(p->d_groups);
   if (p->h_groups) (void)hipHostFree(p->h_groups);
   if (p->groups_uploaded) (void)hipEventDestroy(p->groups_uploaded);

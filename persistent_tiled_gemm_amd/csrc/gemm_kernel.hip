@@ -165,6 +165,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
   __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::LDS];  // two stages
   __shared__ RingRec ring[kRingDepth];
   __shared__ uint32_t gate_ok;
+  __shared__ uint32_t split_last;  // this workgroup finished the last K-chunk of a split tile
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     const uint32_t chunk = ((uint32_t)args.clear_count + gridDim.x - 1u) / gridDim.x;
     const uint32_t first = blockIdx.x * chunk;
     for (uint32_t i = tid; i < chunk; i += (uint32_t)CF::THREADS) {
-      if (first + i < (uint32_t)args.clear_count) args.visits_next[first + i] = 0u;
+      if (first + i < (uint32_t)args.clear_count) args.clear_next[first + i] = 0u;
     }
   }
 
@@ -212,9 +213,9 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
   const uint32_t hwid = read_hw_id();
   const uint32_t xcc = read_xcc_id() % (uint32_t)kXcdRegions;
 
-  // ---- first tile
-  uint32_t ord = 0;       // this worker's tile ordinal
-  uint32_t tile = 0;
+  // ---- first work unit (a whole tile, or one K-chunk of a split tile)
+  uint32_t ord = 0;       // this worker's unit ordinal
+  uint32_t unit = 0;
   bool valid = false;
   // producer state (wave 0, the elected producer, holds the meaningful copy)
   uint32_t next_ord = 1;  // next ordinal to claim
@@ -228,15 +229,24 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       failed = !ok;
     }
     __syncthreads();
-    tile = wave_uniform(ring[0].tile);
+    unit = wave_uniform(ring[0].tile);
     valid = wave_uniform(ring[0].valid) != 0;
   } else {
-    tile = blockIdx.x;
-    valid = tile < (uint32_t)T;
+    unit = blockIdx.x;
+    valid = unit < (uint32_t)T;
   }
 
   while (valid) {
-    // ---- decode the tile id
+    // ---- decode the unit: units below split_base are whole tiles (id = tile id);
+    // unit split_base + q*S + c is K-chunk c of tile split_base + q
+    uint32_t tile = unit;
+    uint32_t chunk = 0;
+    const bool split = !GROUPED && (int32_t)unit >= args.split_base;
+    if (split) {
+      const uint32_t j = unit - (uint32_t)args.split_base;
+      tile = (uint32_t)args.split_base + j / (uint32_t)args.split_chunks;
+      chunk = j % (uint32_t)args.split_chunks;
+    }
     KernelProblem pb;
     int32_t local = (int32_t)tile;
     if constexpr (GROUPED) {
@@ -300,6 +310,9 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     const uint16_t *b_tile = pb.B + n0;
     const int32_t nk = (K + CF::BK - 1) / CF::BK;
     const int32_t full = K / CF::BK;  // k-steps with no K tail
+    // k-steps [kb, ke) of this unit: all of them, or an even share for a K-chunk
+    const int32_t kb = split ? (int32_t)((uint32_t)nk * chunk / (uint32_t)args.split_chunks) : 0;
+    const int32_t ke = split ? (int32_t)((uint32_t)nk * (chunk + 1u) / (uint32_t)args.split_chunks) : nk;
 
     // voffset of load j (A loads first, then B) for k-step kt; chunks outside
     // the matrix (row / column edges, K tail) read as zero via kBufOob.
@@ -423,25 +436,25 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // the prefetch claim is issued claim_lead k-steps before the tile ends (the
     // throttle): late enough not to take work a not-yet-started slot would get,
     // early enough for the atomic's round trip to hide under the MFMAs
-    const int32_t claim_at = nk > args.claim_lead ? nk - args.claim_lead : 0;
-    if (nk == 0) do_claims();
+    const int32_t claim_at = ke - kb > args.claim_lead ? ke - args.claim_lead : kb;
+    if (ke == kb) do_claims();
 
-    if (nk > 0) {
+    if (ke > kb) {
       constexpr int kLoads = CF::A_LOADS + CF::B_LOADS;
       constexpr int kReads = CF::MI + 2 * CF::NI;
       constexpr int kMfma = CF::MI * CF::NI;
-      issue_all(0, 0);
+      issue_all(0, kb);
       wait_vmem_all();
       wg_barrier();
       bf16x8 a0[CF::MI], b0[CF::NI], a1[CF::MI], b1[CF::NI];
       read_frags(0, 0, a0, b0, 0, 0, 0, 0);
-      for (int32_t kt = 0; kt < nk; ++kt) {
+      for (int32_t kt = kb; kt < ke; ++kt) {
         // k-step kt on stage st while k-step kt+1 streams into stage st^1 (the
         // last k-step reloads its own data instead, so no load is out of range);
         // the loads are spread over the first two k-slices, between MFMAs
-        const int st = kt & 1;
+        const int st = (kt - kb) & 1;
         if (kt == claim_at) do_claims();
-        const int32_t kl = kt + 1 < nk ? kt + 1 : kt;
+        const int32_t kl = kt + 1 < ke ? kt + 1 : kt;
         read_frags(st, 1, a1, b1, st ^ 1, kl, 0, kLoads / 2);
         mma(a0, b0);
         interleave<kReads, kMfma>();
@@ -463,10 +476,63 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       }
     }
 
+    // ---- K-chunk of a split tile: publish the partial sum; the workgroup that
+    // completes the tile's last chunk adds all partials in chunk order and writes
+    // C. The order is fixed, so the result does not depend on who finished last.
+    // Partial slots are thread-major per 16-byte group: fully coalesced.
+    bool write_c = true;
+    if (split) {
+      const uint32_t S = (uint32_t)args.split_chunks;
+      const uint32_t q = tile - (uint32_t)args.split_base;
+      f32x4 *slot = reinterpret_cast<f32x4 *>(args.ws) + (size_t)(unit - (uint32_t)args.split_base) * (BM * BN / 4);
+#pragma unroll
+      for (int mi = 0; mi < CF::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < CF::NI; ++ni)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int g = (mi * CF::NI + ni) * 4 + qd;
+            slot[g * CF::THREADS + tid] = f32x4{acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1],
+                                                acc[mi][ni][4 * qd + 2], acc[mi][ni][4 * qd + 3]};
+          }
+      __threadfence();  // release this thread's partial at device scope
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&args.arrivals[q], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        split_last = prev + 1u == S ? 1u : 0u;
+      }
+      __syncthreads();
+      write_c = wave_uniform(split_last) != 0;
+      if (write_c) {
+        __threadfence();  // acquire the other chunks' partials
+        const f32x4 *base = reinterpret_cast<const f32x4 *>(args.ws) + (size_t)q * S * (BM * BN / 4);
+#pragma unroll
+        for (int mi = 0; mi < CF::MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < CF::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
+        for (uint32_t c = 0; c < S; ++c) {
+          const f32x4 *src = base + (size_t)c * (BM * BN / 4);
+#pragma unroll
+          for (int mi = 0; mi < CF::MI; ++mi) {
+#pragma unroll
+            for (int ni = 0; ni < CF::NI; ++ni)
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd) {
+                const f32x4 v = src[((mi * CF::NI + ni) * 4 + qd) * CF::THREADS + tid];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[mi][ni][4 * qd + e] += v[e];
+              }
+          }
+        }
+      }
+    }
+
     // ---- epilogue: fp32 accumulators -> C (lane holds 4 consecutive n of one m)
     const bool interior = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
-    for (int mi = 0; mi < CF::MI; ++mi) {
+    for (int mi = 0; mi < CF::MI && write_c; ++mi) {
       const int32_t m = m0 + (int32_t)(wm * CF::WM + mi * 32 + (lane & 31u));
       float *crow = pb.C + (size_t)m * (size_t)N;
 #pragma unroll
@@ -501,9 +567,11 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     if (tid == 0) {
       const uint64_t t1 = clock_core();
       const uint64_t r1 = clock_wall();
-      if ((int32_t)tile < args.log_cap) {
+      if ((int32_t)unit < args.log_cap) {
         TileRecDev rec;
         rec.tile = tile;
+        rec.kb = (uint32_t)kb;
+        rec.ke = (uint32_t)ke;
         rec.worker = blockIdx.x;
         rec.hw_id = hwid;
         rec.xcc_id = xcc;
@@ -511,8 +579,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         rec.t1 = t1;
         rec.r0 = r0;
         rec.r1 = r1;
-        args.log[tile] = rec;
-        __hip_atomic_fetch_add(&args.visits[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        args.log[unit] = rec;
+        __hip_atomic_fetch_add(&args.visits[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
 
@@ -522,15 +590,15 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       const RingRec rec = ring[(ord + 1) % (uint32_t)args.ring_depth];
       const uint32_t seq = wave_uniform(rec.seq);
       valid = wave_uniform(rec.valid) != 0;
-      tile = wave_uniform(rec.tile);
+      unit = wave_uniform(rec.tile);
       if (seq != ord + 1) {
         // the ring protocol was violated: stop this worker and flag it
         if (tid == 0) __hip_atomic_fetch_or(&args.ctrl->error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         valid = false;
       }
     } else if constexpr (MODE == kStatic) {
-      tile += (uint32_t)args.P;
-      valid = tile < (uint32_t)T;
+      unit += (uint32_t)args.P;
+      valid = unit < (uint32_t)T;
     } else {
       valid = false;
     }

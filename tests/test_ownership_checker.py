@@ -61,3 +61,49 @@ def test_region_rule_for_partitioned_claims():
     assert not check_ownership("dynamic", 5, tile, worker, start, end, visits, regions=2)
     bad = np.array([2, 0, 4, 1, 3])                                                    # region 0 out of order
     assert check_ownership("dynamic", 5, bad, worker, start, end, visits, regions=2)
+
+
+def test_k_cover_accepts_partitions_and_rejects_planted_errors():
+    from oracle.ownership import check_k_cover
+    # three whole tiles and tile 3 cut into chunks [0,128) [128,320) [320,512)
+    tile = np.array([0, 1, 2, 3, 3, 3])
+    kb = np.array([0, 0, 0, 0, 128, 320])
+    ke = np.array([512, 512, 512, 128, 320, 512])
+    assert check_k_cover(tile, kb, ke, 4, 512) == []
+    # order of the records does not matter
+    p = np.array([5, 0, 3, 1, 4, 2])
+    assert check_k_cover(tile[p], kb[p], ke[p], 4, 512) == []
+    # a gap, an overlap, a short cover, a missing tile, a duplicated chunk
+    assert check_k_cover(tile, kb, np.array([512, 512, 512, 120, 320, 512]), 4, 512)
+    assert check_k_cover(tile, np.array([0, 0, 0, 0, 100, 320]), ke, 4, 512)
+    assert check_k_cover(tile, kb, np.array([512, 512, 512, 128, 320, 500]), 4, 512)
+    assert check_k_cover(tile[:-3], kb[:-3], ke[:-3], 4, 512)
+    assert check_k_cover(np.r_[tile, 3], np.r_[kb, 320], np.r_[ke, 512], 4, 512)
+    # K == 0: each tile is one empty unit
+    assert check_k_cover(np.arange(3), np.zeros(3), np.zeros(3), 3, 0) == []
+    # per-tile K (grouped problems)
+    assert check_k_cover(np.array([0, 1]), np.array([0, 0]), np.array([64, 128]), 2, np.array([64, 128])) == []
+    assert check_k_cover(np.array([0, 1]), np.array([0, 0]), np.array([64, 64]), 2, np.array([64, 128]))
+
+
+def test_split_units_decomposition():
+    from oracle.ownership import check_k_cover, split_units
+    # 257 tiles on 256 workers, 64 k-steps, up to 8 chunks: the odd tile becomes 8 units of 8 k-steps
+    u = split_units(257, 256, 64, 8)
+    assert len(u) == 256 + 8
+    assert u[:256] == [(t, 0, 64) for t in range(256)]
+    assert u[256:] == [(256, 8 * c, 8 * c + 8) for c in range(8)]
+    # chunk count limited by idle workers (r = 100 -> 256 // 100 = 2) and by K (nk // 4)
+    assert len(split_units(356, 256, 64, 8)) == 256 + 100 * 2
+    assert len(split_units(257, 256, 12, 8)) == 256 + 3          # nk // 4 = 3
+    assert split_units(257, 256, 7, 8) == [(t, 0, 7) for t in range(257)]   # one chunk only: no split
+    # no partial wave, fewer tiles than workers, splitting off
+    assert split_units(512, 256, 64, 8) == [(t, 0, 64) for t in range(512)]
+    assert split_units(100, 256, 64, 8) == [(t, 0, 64) for t in range(100)]
+    assert split_units(257, 256, 64, 0) == [(t, 0, 64) for t in range(257)]
+    # uneven division of the k-steps still covers [0, nk) exactly
+    for T, P, nk, s in ((257, 256, 30, 7), (14, 5, 13, 3), (1030, 256, 100, 64)):
+        u = split_units(T, P, nk, s)
+        t = np.array([x[0] for x in u]); b = np.array([x[1] for x in u]); e = np.array([x[2] for x in u])
+        assert check_k_cover(t, b, e, T, nk) == []
+        assert all(x[2] - x[1] >= 4 for x in u if x[2] - x[1] != nk)
