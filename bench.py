@@ -174,6 +174,16 @@ def run_tail_sections(ptg, torch, stream, khz, square):
             kt = ks[ran["problem"]] / 64.0
             alpha, beta = np.polyfit(kt, dur, 1)
     res["cost_fit_us"] = {"per_kstep": float(alpha), "fixed": float(beta)}
+    # the dynamic scheduler handing out the longest-K problems first
+    lplan = ptg.gemm_create(tile_edge=256, log_capacity=1024, group_order=1)
+    ptg.gemm_run_grouped(As, Bs, Cs, lplan, mode="dynamic", stream=stream)
+    ms_ev = time_runs(lambda: ptg.gemm_run_grouped(As, Bs, Cs, lplan, mode="dynamic", stream=stream), 5, 1, stream)
+    ptg.gemm_run_grouped(As, Bs, Cs, lplan, mode="dynamic", stream=stream)
+    ms = makespan_from_log(ptg.gemm_read_log(lplan), khz)
+    ms["kernel_ms"] = ms_ev
+    ms["tflops"] = w.flops / (ms_ev * 1e-3) / 1e12
+    res["dynamic_longest_k_first"] = ms
+    lplan.destroy()
     res["dynamic_beats_static"] = bool(res["dynamic"]["makespan_us"] < res["static"]["makespan_us"])
     out["grouped_uneven"] = res
     plan.destroy()

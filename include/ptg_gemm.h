@@ -124,6 +124,13 @@ typedef enum gemm_sched_mode {
  *                   Workers per wave: the static mode's P, else occupancy x
  *                   CUs. gemm_create then reserves the partial-sum scratch:
  *                   bm x bn x 4 bytes per worker of one wave.
+ *   group_order     grouped runs only: the order work units are handed out in.
+ *                   0 = problem after problem, as given. 1 = problems with the
+ *                   longest K first (stable for equal K): a tile's cost grows
+ *                   with its K, and handing out the costly tiles first leaves
+ *                   the cheap ones to fill the end of the run (the longest-
+ *                   processing-time rule). Tile ids in the log keep the
+ *                   as-given numbering either way; unit ids follow the order.
  */
 typedef struct gemm_tile_desc {
   int32_t bm, bn, bk;
@@ -140,6 +147,7 @@ typedef struct gemm_tile_desc {
   int32_t max_groups;
   int32_t device;
   int32_t tail_split;
+  int32_t group_order;
 } gemm_tile_desc;
 
 /* Opaque plan: the tile_cfg argument of gemm_run. Owns all library scratch. */

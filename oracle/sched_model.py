@@ -54,7 +54,7 @@ import math
 from collections import deque
 from typing import Dict, List, Optional, Sequence
 
-__all__ = ["TileRun", "WorkerRun", "Schedule", "simulate", "MODES"]
+__all__ = ["TileRun", "WorkerRun", "Schedule", "simulate", "lpt_claim_order", "MODES"]
 
 MODES = ("nonpersistent", "static", "dynamic")
 
@@ -274,3 +274,24 @@ def simulate(costs: Sequence[float], mode: str, slots: Optional[int] = None,
         makespan = 0.0
     span = (max(w.exit for w in workers.values()) - min(w.dispatch for w in workers.values())) if workers else 0.0
     return Schedule(mode, tiles, workers, makespan, span)  # type: ignore[arg-type]
+
+
+def lpt_claim_order(problem_costs: Sequence[float], tiles_per_problem: Sequence[int]) -> List[int]:
+    """Tile ids (problems numbered as given, tiles of problem g consecutive) in
+    longest-processing-time claim order: problems by non-increasing per-tile cost,
+    equal costs in the given problem order, each problem's tiles in their own order.
+
+    [SKILL] (section "E - executable steps", choosing the scheduling mode) sends
+    work of uneven cost to the dynamic scheduler; the order in which that work
+    is handed out is not on the pages. Giving the costliest work out first is
+    the classic longest-processing-time list-scheduling rule (Graham 1969),
+    whose makespan is at most (4/3 - 1/(3S)) of the optimum on S slots.
+    """
+    starts = [0]
+    for n in tiles_per_problem:
+        starts.append(starts[-1] + int(n))
+    order = sorted(range(len(problem_costs)), key=lambda g: (-float(problem_costs[g]), g))
+    out: List[int] = []
+    for g in order:
+        out.extend(range(starts[g], starts[g + 1]))
+    return out

@@ -51,7 +51,7 @@ class PtgError(RuntimeError):
 class TileDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bm", "bn", "bk", "ring_depth", "claims_ahead", "claim_lead", "claim_policy", "raster", "raster_group", "static_workers",
-        "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device", "tail_split")]
+        "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device", "tail_split", "group_order")]
 
 
 class TileRec(ctypes.Structure):

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <climits>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -54,6 +55,7 @@ struct gemm_plan {
   int32_t last_mode = -1;
   std::vector<int32_t> last_tile_start;  // per problem (grouped), for log decoding
   std::vector<int32_t> last_k;           // K per problem, for log decoding
+  std::vector<std::pair<int32_t, int32_t>> last_unit_map;  // grouped, claim order: (unit_start, tile_start)
   std::string last_error;
 };
 
@@ -208,6 +210,7 @@ gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t de
   out->max_groups = 1024;
   out->device = device;
   out->tail_split = 0;
+  out->group_order = 0;
   return GEMM_OK;
 }
 
@@ -221,7 +224,8 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (d.claim_lead < 0 || d.claim_policy < 0 || d.claim_policy > 1) return GEMM_E_INVALID_ARG;
   if (d.raster < 0 || d.raster > 1 || (d.raster == 1 && d.raster_group < 1)) return GEMM_E_INVALID_ARG;
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
-      d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT)
+      d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT || d.group_order < 0 ||
+      d.group_order > 1)
     return GEMM_E_INVALID_ARG;
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -328,10 +332,12 @@ gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t 
   args.single.tiles_m = (int32_t)tm;
   args.single.tiles_n = (int32_t)tn;
   args.single.tile_start = 0;
+  args.single.unit_start = 0;
   args.groups = nullptr;
   args.G = 1;
   p->last_tile_start.assign(1, 0);
   p->last_k.assign(1, (int32_t)K);
+  p->last_unit_map.clear();
   return launch(p, sched_mode, false, args, tiles, K, static_cast<hipStream_t>(stream));
 }
 
@@ -359,6 +365,7 @@ gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const 
     q.tiles_m = (int32_t)ceil_div(M[g], p->desc.bm);
     q.tiles_n = (int32_t)ceil_div(N[g], p->desc.bn);
     q.tile_start = (int32_t)tiles;
+    q.unit_start = (int32_t)tiles;
     starts[(size_t)g] = (int32_t)tiles;
     ks[(size_t)g] = (int32_t)K[g];
     tiles += (int64_t)q.tiles_m * q.tiles_n;
@@ -367,31 +374,47 @@ gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const 
   gemm_status st = check_current_device(p);
   if (st != GEMM_OK) return st;
   if (tiles == 0) return GEMM_OK;
+  // claim order: problems as given, or longest K first (every tile of a problem
+  // costs about K; handing out the costly tiles first keeps the short ones for
+  // the end, where they fill the gaps: longest-processing-time order). The table
+  // goes to the device in claim order; tile ids keep the call-order numbering.
+  std::vector<KernelProblem> table = probs;
+  if (p->desc.group_order == 1) {
+    std::stable_sort(table.begin(), table.end(),
+                     [](const KernelProblem &a, const KernelProblem &b) { return a.K > b.K; });
+    int32_t u = 0;
+    for (KernelProblem &q : table) {
+      q.unit_start = u;
+      u += q.tiles_m * q.tiles_n;
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool same = p->last_groups.size() == probs.size() &&
-                    std::memcmp(p->last_groups.data(), probs.data(), sizeof(KernelProblem) * probs.size()) == 0;
+  const bool same = p->last_groups.size() == table.size() &&
+                    std::memcmp(p->last_groups.data(), table.data(), sizeof(KernelProblem) * table.size()) == 0;
   if (!same) {
     // the pinned staging may still be the source of an earlier upload
     if (p->groups_event_pending) {
       hipError_t e = hipEventSynchronize(p->groups_uploaded);
       if (e != hipSuccess) return hip_fail(p, e, "hipEventSynchronize(groups)");
     }
-    std::memcpy(p->h_groups, probs.data(), sizeof(KernelProblem) * probs.size());
-    hipError_t e = hipMemcpyAsync(p->d_groups, p->h_groups, sizeof(KernelProblem) * probs.size(),
+    std::memcpy(p->h_groups, table.data(), sizeof(KernelProblem) * table.size());
+    hipError_t e = hipMemcpyAsync(p->d_groups, p->h_groups, sizeof(KernelProblem) * table.size(),
                                   hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(p, e, "hipMemcpyAsync(groups)");
     e = hipEventRecord(p->groups_uploaded, s);
     if (e != hipSuccess) return hip_fail(p, e, "hipEventRecord(groups)");
     p->groups_event_pending = true;
-    p->last_groups = probs;
+    p->last_groups = table;
   }
   KernelArgs args;
   std::memset(&args, 0, sizeof(args));
-  args.single = probs[0];
+  args.single = table[0];
   args.groups = p->d_groups;
   args.G = G;
   p->last_tile_start = starts;
   p->last_k = ks;
+  p->last_unit_map.clear();
+  for (const KernelProblem &q : table) p->last_unit_map.emplace_back(q.unit_start, q.tile_start);
   return launch(p, sched_mode, true, args, tiles, 0, s);
 }
 
@@ -428,6 +451,11 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
     if ((int64_t)i >= p->last_split_base) {
       tile = p->last_split_base + ((int64_t)i - p->last_split_base) / S;
       chunk = ((int64_t)i - p->last_split_base) % S;
+    } else if (!p->last_unit_map.empty()) {
+      const auto &um = p->last_unit_map;
+      const auto it = std::upper_bound(um.begin(), um.end(), std::make_pair((int32_t)i, INT32_MAX));
+      const auto &e0 = *(it - 1);
+      tile = e0.second + ((int64_t)i - e0.first);
     }
     const auto &ts = p->last_tile_start;
     const size_t g = (size_t)(std::upper_bound(ts.begin(), ts.end(), (int32_t)tile) - ts.begin() - 1);

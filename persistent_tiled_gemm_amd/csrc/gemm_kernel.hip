@@ -262,7 +262,9 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       pb.tiles_m = (int32_t)wave_uniform((uint32_t)pb.tiles_m);
       pb.tiles_n = (int32_t)wave_uniform((uint32_t)pb.tiles_n);
       pb.tile_start = (int32_t)wave_uniform((uint32_t)pb.tile_start);
-      local -= pb.tile_start;
+      pb.unit_start = (int32_t)wave_uniform((uint32_t)pb.unit_start);
+      local -= pb.unit_start;
+      tile = (uint32_t)(pb.tile_start + local);  // the tile id in call-order numbering
     } else {
       pb = args.single;
     }

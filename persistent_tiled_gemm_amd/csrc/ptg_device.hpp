@@ -117,12 +117,13 @@ __device__ __forceinline__ void decode_tile(int32_t t, int32_t tiles_m, int32_t 
   n_t = r / gm;
 }
 
-// Which problem of a grouped launch owns global tile id t (tile_start ascending).
-__device__ __forceinline__ int32_t find_problem(const KernelProblem *probs, int32_t G, int32_t t) {
+// Which entry of a grouped launch's table owns work unit u (unit_start ascending:
+// the table is in claim order).
+__device__ __forceinline__ int32_t find_problem(const KernelProblem *probs, int32_t G, int32_t u) {
   int32_t lo = 0, hi = G - 1;
   while (lo < hi) {
     const int32_t mid = (lo + hi + 1) >> 1;
-    if (probs[mid].tile_start <= t) lo = mid; else hi = mid - 1;
+    if (probs[mid].unit_start <= u) lo = mid; else hi = mid - 1;
   }
   return lo;
 }

@@ -14,7 +14,8 @@ struct KernelProblem {
   float *C;            // M x N fp32, row-major
   int32_t M, N, K;
   int32_t tiles_m, tiles_n;
-  int32_t tile_start;  // first global tile id of this problem
+  int32_t tile_start;  // first global tile id of this problem (problems numbered in call order)
+  int32_t unit_start;  // first work unit of this problem (units numbered in claim order)
 };
 
 // Tile regions of the XCD-partitioned claim policy: region x holds the tiles

@@ -117,3 +117,34 @@ def test_tail_split_shortens_the_partial_wave():
     assert res["split"][0] / t >= model_split * 0.9
     whole.destroy()
     split.destroy()
+
+
+def test_grouped_longest_k_first_against_model():
+    torch = torch_mod()
+    w = make_workload("grouped_uneven")
+    As = [ptg.bf16_from_bits(q.a_bits) for q in w.problems]
+    Bs = [ptg.bf16_from_bits(q.b_bits) for q in w.problems]
+    Cs = [torch.empty((q.M, q.N), dtype=torch.float32, device="cuda") for q in w.problems]
+    ks = np.array([q.K for q in w.problems])
+    spans = {}
+    for order in (0, 1):
+        plan = ptg.gemm_create(tile_edge=256, log_capacity=1024, group_order=order)
+        khz = ptg.gemm_plan_info_get(plan)["wallclock_khz"]
+        say(f"case grouped claim order {order}")
+        for _ in range(3):
+            ptg.gemm_run_grouped(As, Bs, Cs, plan, mode="dynamic")
+        torch.cuda.synchronize()
+        span, _, ran = _span(ptg.gemm_read_log(plan), khz)
+        spans[order] = span
+        if order == 0:
+            dur = (ran["r1"] - ran["r0"]).astype(np.float64) / khz * 1e3
+            alpha, beta = np.polyfit(ks[ran["problem"]] / 64.0, dur, 1)
+        plan.destroy()
+    costs = [alpha * (k / 64.0) + beta for k in ks]
+    from oracle.sched_model import lpt_claim_order
+    model_given = simulate([costs[t // 16] for t in range(1024)], "dynamic", slots=256).makespan
+    model_lpt = simulate([costs[t // 16] for t in lpt_claim_order(costs, [16] * 64)], "dynamic", slots=256).makespan
+    say(f"  as given {spans[0]:.1f} us (model {model_given:.1f}), longest K first {spans[1]:.1f} us "
+        f"(model {model_lpt:.1f})")
+    assert 0.8 * model_lpt <= spans[1] <= 1.3 * model_lpt
+    assert spans[1] < spans[0]

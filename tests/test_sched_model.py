@@ -175,3 +175,38 @@ def test_late_slots_exit_at_once():
         if not w.tiles:
             assert w.exit == w.dispatch  # one failed claim, nothing else
             assert w.claims == 1
+
+
+def test_lpt_claim_order_definition():
+    from oracle.sched_model import lpt_claim_order
+    # problems 0..3 with 2, 1, 3, 1 tiles and per-tile costs 5, 9, 5, 1
+    order = lpt_claim_order([5, 9, 5, 1], [2, 1, 3, 1])
+    assert order == [2, 0, 1, 3, 4, 5, 6]
+    # a permutation of all tiles, costs non-increasing along it
+    rng = np.random.default_rng(4)
+    costs = rng.integers(1, 17, size=40).tolist()
+    n = rng.integers(1, 5, size=40).tolist()
+    order = lpt_claim_order(costs, n)
+    assert sorted(order) == list(range(sum(n)))
+    owner = np.repeat(np.arange(40), n)
+    seq = [costs[owner[t]] for t in order]
+    assert all(a >= b for a, b in zip(seq, seq[1:]))
+
+
+def test_lpt_order_meets_grahams_bound_and_helps_uneven_costs():
+    from oracle.sched_model import lpt_claim_order
+    # brute force on tiny instances: greedy dynamic over the LPT order stays within 4/3 - 1/(3S) of optimum
+    rng = np.random.default_rng(7)
+    for _ in range(30):
+        S = int(rng.integers(2, 4))
+        c = rng.integers(1, 10, size=int(rng.integers(3, 8))).tolist()
+        order = lpt_claim_order(c, [1] * len(c))
+        got = simulate([c[t] for t in order], "dynamic", slots=S).makespan
+        best = min(max(sum(c[j] for j in range(len(c)) if a[j] == s) for s in range(S))
+                   for a in itertools.product(range(S), repeat=len(c)))
+        assert got <= (4 / 3 - 1 / (3 * S)) * best + 1e-9
+    # the classic bad case for as-given order: short jobs first, one long job last
+    c = [1] * 8 + [8]
+    assert simulate(c, "dynamic", slots=4).makespan == 10
+    order = lpt_claim_order(c, [1] * 9)
+    assert simulate([c[t] for t in order], "dynamic", slots=4).makespan == 8
