@@ -317,8 +317,10 @@ def main():
     if not args.no_modes:
         other = dict(fields, claim_policy=1 - args.claim_policy)
         plan_other = ptg.gemm_create(**other)
+        plan_group = ptg.gemm_create(**dict(fields, claim_group=4, raster=1, raster_group=2))
         runs = [("nonpersistent", "nonpersistent", plan), ("static", "static", plan), ("dynamic", "dynamic", plan),
-                ("dynamic_single_counter" if args.claim_policy == 1 else "dynamic_xcd_counters", "dynamic", plan_other)]
+                ("dynamic_single_counter" if args.claim_policy == 1 else "dynamic_xcd_counters", "dynamic", plan_other),
+                ("dynamic_claim_groups_2x2", "dynamic", plan_group)]
         for name, mode, pl in runs:
             m_ms = time_runs(lambda: ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream), max(5, args.steps // 2),
                              2, stream)
@@ -329,6 +331,7 @@ def main():
             if mk:
                 modes[name].update(makespan_us=mk["makespan_us"], tile_median_us=mk["tile_median_us"])
         plan_other.destroy()
+        plan_group.destroy()
         # context only: the vendor library's bf16 GEMM at the same shape (torch.matmul -> hipBLASLt). It
         # writes a bf16 C (half of our fp32 C bytes), so it is a near, not an exact, comparison.
         v_ms = time_runs(lambda: torch.matmul(A, B), max(5, args.steps // 2), 2, stream)

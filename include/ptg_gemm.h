@@ -87,6 +87,7 @@ typedef enum gemm_sched_mode {
 #define GEMM_MAX_M (1 << 30)
 #define GEMM_MAX_TILES (1 << 30)
 #define GEMM_MAX_TAIL_SPLIT 64
+#define GEMM_MAX_CLAIM_GROUP 16
 
 /*
  * Plan descriptor (a value type; gemm_create copies it). Fields:
@@ -131,6 +132,14 @@ typedef enum gemm_sched_mode {
  *                   the cheap ones to fill the end of the run (the longest-
  *                   processing-time rule). Tile ids in the log keep the
  *                   as-given numbering either way; unit ids follow the order.
+ *   claim_group     single GEMMs only: tiles per work unit (0 or 1 = one tile;
+ *                   up to GEMM_MAX_CLAIM_GROUP). One claim (one static step,
+ *                   one non-persistent block) then takes g consecutive tile ids
+ *                   of the raster order, run back to back by one worker: with
+ *                   the grouped-M raster of height h and g = 2h the unit is a
+ *                   2 x h block of tiles sharing A and B panels, the claim-sized
+ *                   counterpart of a cluster. Exclusive with tail_split (a
+ *                   claim group wins).
  */
 typedef struct gemm_tile_desc {
   int32_t bm, bn, bk;
@@ -148,23 +157,26 @@ typedef struct gemm_tile_desc {
   int32_t device;
   int32_t tail_split;
   int32_t group_order;
+  int32_t claim_group;
 } gemm_tile_desc;
 
 /* Opaque plan: the tile_cfg argument of gemm_run. Owns all library scratch. */
 typedef struct gemm_plan *gemm_tile_cfg;
 
 /*
- * One work-unit log record (host copy), indexed by unit id. Without tail
- * splitting units are tiles (unit == tile). unit: the work-unit id the
- * schedulers hand out; tile: output tile id in raster order (grouped: ids of
- * problem g follow those of problems < g); k_begin/k_end: the K range [k_begin,
- * k_end) the unit accumulated (the whole K for a whole tile); worker: launch
- * slot (blockIdx.x) that ran it; hw_id / xcc_id: raw HW_ID and XCC_ID hardware
- * registers of the wave that ran it; t0/t1: s_memtime at unit start / after
- * its stores were issued; r0/r1: the same moments on the constant-rate
- * s_memrealtime clock (rate: gemm_plan_info's wallclock_khz); visits: how many
- * times the unit was finished (exactly-once => 1); problem: grouped problem
- * index (0 otherwise).
+ * One log record (host copy) per work item, indexed by item id. An item is a
+ * whole tile or one K-chunk of a split tile; without tail splitting the item
+ * id is the tile id (in claim order for grouped runs with group_order = 1).
+ * unit: the work unit (claim, static step, non-persistent block) that covered
+ * the item, equal to the item id unless claim groups are on; tile: output
+ * tile id in raster order (grouped: ids of problem g follow those of problems
+ * < g); k_begin/k_end: the K range [k_begin, k_end) the item accumulated (the
+ * whole K for a whole tile); worker: launch slot (blockIdx.x) that ran it;
+ * hw_id / xcc_id: raw HW_ID and XCC_ID hardware registers of the wave that ran
+ * it; t0/t1: s_memtime at item start / after its stores were issued; r0/r1:
+ * the same moments on the constant-rate s_memrealtime clock (rate:
+ * gemm_plan_info's wallclock_khz); visits: how many times the item was
+ * finished (exactly-once => 1); problem: grouped problem index (0 otherwise).
  */
 typedef struct gemm_tile_rec {
   uint32_t tile, worker, hw_id, xcc_id;
@@ -181,9 +193,11 @@ typedef struct gemm_plan_info {
   int32_t static_workers;    /* P the static mode uses for a large problem */
   int64_t wallclock_khz;     /* s_memrealtime rate */
   int64_t last_tiles;        /* T of the last run */
-  int64_t last_units;        /* work units of the last run (== last_tiles unless split) */
+  int64_t last_units;        /* work units handed out in the last run */
+  int64_t last_items;        /* work items (log records) of the last run: tiles plus split chunks */
   int64_t last_split_base;   /* first split tile (== last_tiles when nothing was split) */
   int32_t last_split_chunks; /* K-chunks per split tile (1 when nothing was split) */
+  int32_t last_claim_group;  /* tiles per unit of the last run */
   int64_t last_grid;         /* grid size of the last run */
   int32_t last_mode;         /* scheduler of the last run (-1 before the first) */
   int32_t lds_bytes;         /* LDS per workgroup */

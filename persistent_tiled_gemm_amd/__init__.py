@@ -51,7 +51,7 @@ class PtgError(RuntimeError):
 class TileDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bm", "bn", "bk", "ring_depth", "claims_ahead", "claim_lead", "claim_policy", "raster", "raster_group", "static_workers",
-        "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device", "tail_split", "group_order")]
+        "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device", "tail_split", "group_order", "claim_group")]
 
 
 class TileRec(ctypes.Structure):
@@ -65,8 +65,9 @@ class TileRec(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("device", ctypes.c_int32), ("cu_count", ctypes.c_int32), ("occupancy", ctypes.c_int32),
                 ("static_workers", ctypes.c_int32), ("wallclock_khz", ctypes.c_int64),
-                ("last_tiles", ctypes.c_int64), ("last_units", ctypes.c_int64), ("last_split_base", ctypes.c_int64),
-                ("last_split_chunks", ctypes.c_int32), ("last_grid", ctypes.c_int64), ("last_mode", ctypes.c_int32),
+                ("last_tiles", ctypes.c_int64), ("last_units", ctypes.c_int64), ("last_items", ctypes.c_int64), ("last_split_base", ctypes.c_int64),
+                ("last_split_chunks", ctypes.c_int32), ("last_claim_group", ctypes.c_int32),
+                ("last_grid", ctypes.c_int64), ("last_mode", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32)]
 
 

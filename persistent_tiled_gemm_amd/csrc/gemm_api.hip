@@ -49,8 +49,10 @@ struct gemm_plan {
   bool has_run = false;
   int64_t last_tiles = 0;
   int64_t last_units = 0;
+  int64_t last_items = 0;
   int64_t last_split_base = 0;
   int32_t last_split_chunks = 0;
+  int32_t last_claim_group = 1;
   int64_t last_grid = 0;
   int32_t last_mode = -1;
   std::vector<int32_t> last_tile_start;  // per problem (grouped), for log decoding
@@ -101,15 +103,22 @@ constexpr size_t kVisitsOffset = sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)
 // Fewest k-steps a K-chunk of a split tile gets.
 constexpr int64_t kMinChunkSteps = 4;
 
-// Work units of a run: T whole tiles, or, with tail splitting on, the tiles
+// Work items of a run: T whole tiles, or, with tail splitting on, the tiles
 // that fill whole waves of `workers` plus the r = T mod workers tiles of the
 // partial last wave, each split into S K-chunks (S <= tail_split, <= workers / r
 // so the chunks fit the idle workers, and >= kMinChunkSteps k-steps each).
-void plan_units(const gemm_plan *p, bool grouped, int32_t mode, int64_t tiles, int64_t K, int64_t *units,
-                int64_t *split_base, int32_t *chunks) {
-  *units = tiles;
+// Work units (what one claim, static step or non-persistent block takes) are
+// the items, or with claim groups g consecutive tiles (nothing is then split).
+void plan_units(const gemm_plan *p, bool grouped, int32_t mode, int64_t tiles, int64_t K, int64_t *items,
+                int64_t *split_base, int32_t *chunks, int32_t *group) {
+  *items = tiles;
   *split_base = tiles;
   *chunks = 1;
+  *group = 1;
+  if (!grouped && p->desc.claim_group > 1) {
+    *group = p->desc.claim_group;
+    return;
+  }
   if (grouped || p->desc.tail_split < 2 || p->ws_tiles == 0) return;
   const int64_t workers =
       mode == GEMM_SCHED_STATIC ? (int64_t)p->static_workers : (int64_t)p->occupancy * p->cu_count;
@@ -121,19 +130,22 @@ void plan_units(const gemm_plan *p, bool grouped, int32_t mode, int64_t tiles, i
   if (S < 2) return;
   *split_base = tiles - r;
   *chunks = (int32_t)S;
-  *units = tiles - r + r * S;
+  *items = tiles - r + r * S;
 }
 
 gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, int64_t tiles, int64_t K,
                    hipStream_t s) {
   if (mode < GEMM_SCHED_NONPERSISTENT || mode > GEMM_SCHED_DYNAMIC) return GEMM_E_INVALID_ARG;
-  int64_t units = tiles, split_base = tiles;
-  int32_t chunks = 1;
-  plan_units(p, grouped, mode, tiles, K, &units, &split_base, &chunks);
-  if (units > GEMM_MAX_TILES) return GEMM_E_SHAPE;
+  int64_t items = tiles, split_base = tiles;
+  int32_t chunks = 1, group = 1;
+  plan_units(p, grouped, mode, tiles, K, &items, &split_base, &chunks, &group);
+  if (items > GEMM_MAX_TILES) return GEMM_E_SHAPE;
+  const int64_t units = ceil_div(items, group);
   int64_t grid = units;
   if (mode == GEMM_SCHED_STATIC) grid = std::min<int64_t>(units, p->static_workers);
   args.T = (int32_t)units;
+  args.items = (int32_t)items;
+  args.claim_group = group;
   args.split_base = (int32_t)split_base;
   args.split_chunks = chunks;
   args.ws = p->d_ws;
@@ -165,8 +177,10 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   p->has_run = true;
   p->last_tiles = tiles;
   p->last_units = units;
+  p->last_items = items;
   p->last_split_base = split_base;
   p->last_split_chunks = chunks;
+  p->last_claim_group = group;
   p->last_grid = grid;
   p->last_mode = mode;
   return GEMM_OK;
@@ -211,6 +225,7 @@ gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t de
   out->device = device;
   out->tail_split = 0;
   out->group_order = 0;
+  out->claim_group = 1;
   return GEMM_OK;
 }
 
@@ -225,7 +240,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (d.raster < 0 || d.raster > 1 || (d.raster == 1 && d.raster_group < 1)) return GEMM_E_INVALID_ARG;
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
       d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT || d.group_order < 0 ||
-      d.group_order > 1)
+      d.group_order > 1 || d.claim_group < 0 || d.claim_group > GEMM_MAX_CLAIM_GROUP)
     return GEMM_E_INVALID_ARG;
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -425,7 +440,7 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
   if (!p->has_run || p->desc.log_capacity == 0) return GEMM_OK;
   hipError_t e = hipStreamSynchronize(p->last_stream);
   if (e != hipSuccess) return hip_fail(p, e, "hipStreamSynchronize");
-  const size_t n = (size_t)std::min<int64_t>(p->last_units, p->desc.log_capacity);
+  const size_t n = (size_t)std::min<int64_t>(p->last_items, p->desc.log_capacity);
   const size_t m = std::min(n, cap);
   std::vector<TileRecDev> recs(m);
   std::vector<uint32_t> visits(m);
@@ -444,10 +459,10 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
     gemm_tile_rec &r = host_out[i];
     std::memset(&r, 0, sizeof(r));
     r.visits = visits[i];
-    r.unit = (uint32_t)i;
-    // the unit's tile and K range as the launch planned them
+    // the item's tile, K range and unit as the launch planned them
     int64_t tile = (int64_t)i, chunk = 0;
     const int64_t S = p->last_split_chunks;
+    r.unit = (uint32_t)((int64_t)i / p->last_claim_group);
     if ((int64_t)i >= p->last_split_base) {
       tile = p->last_split_base + ((int64_t)i - p->last_split_base) / S;
       chunk = ((int64_t)i - p->last_split_base) % S;
@@ -475,6 +490,7 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
     r.k_begin = (uint32_t)std::min((int64_t)recs[i].kb * bk, Kg);
     r.k_end = (uint32_t)std::min((int64_t)recs[i].ke * bk, Kg);
     r.tile = recs[i].tile;
+    r.unit = recs[i].unit;
     r.worker = recs[i].worker;
     r.hw_id = recs[i].hw_id;
     r.xcc_id = recs[i].xcc_id;
@@ -502,8 +518,10 @@ gemm_status gemm_plan_info_get(gemm_tile_cfg tile_cfg, gemm_plan_info *out) {
   out->wallclock_khz = p->wallclock_khz;
   out->last_tiles = p->last_tiles;
   out->last_units = p->last_units;
+  out->last_items = p->last_items;
   out->last_split_base = p->last_split_base;
   out->last_split_chunks = p->last_split_chunks;
+  out->last_claim_group = p->last_claim_group;
   out->last_grid = p->last_grid;
   out->last_mode = p->last_mode;
   out->lds_bytes = p->lds_bytes;

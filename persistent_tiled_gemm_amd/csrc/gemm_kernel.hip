@@ -236,14 +236,19 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     valid = unit < (uint32_t)T;
   }
 
+  uint32_t sub = 0;  // the current item's place in its unit (claim groups)
   while (valid) {
-    // ---- decode the unit: units below split_base are whole tiles (id = tile id);
-    // unit split_base + q*S + c is K-chunk c of tile split_base + q
-    uint32_t tile = unit;
+    // ---- the work item: unit u covers items [u g, u g + g) (g = claim_group, 1
+    // unless claim groups are on); items below split_base are whole tiles (id =
+    // tile id), item split_base + q*S + c is K-chunk c of tile split_base + q
+    const uint32_t g = (uint32_t)args.claim_group;
+    const uint32_t item = unit * g + sub;
+    const bool last_sub = sub + 1 >= min(g, (uint32_t)args.items - unit * g);
+    uint32_t tile = item;
     uint32_t chunk = 0;
-    const bool split = !GROUPED && (int32_t)unit >= args.split_base;
+    const bool split = !GROUPED && (int32_t)item >= args.split_base;
     if (split) {
-      const uint32_t j = unit - (uint32_t)args.split_base;
+      const uint32_t j = item - (uint32_t)args.split_base;
       tile = (uint32_t)args.split_base + j / (uint32_t)args.split_chunks;
       chunk = j % (uint32_t)args.split_chunks;
     }
@@ -438,8 +443,9 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // the prefetch claim is issued claim_lead k-steps before the tile ends (the
     // throttle): late enough not to take work a not-yet-started slot would get,
     // early enough for the atomic's round trip to hide under the MFMAs
-    const int32_t claim_at = ke - kb > args.claim_lead ? ke - args.claim_lead : kb;
-    if (ke == kb) do_claims();
+    // claims for the next unit go out during the unit's last item only
+    const int32_t claim_at = !last_sub ? -1 : ke - kb > args.claim_lead ? ke - args.claim_lead : kb;
+    if (ke == kb && last_sub) do_claims();
 
     if (ke > kb) {
       constexpr int kLoads = CF::A_LOADS + CF::B_LOADS;
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     if (split) {
       const uint32_t S = (uint32_t)args.split_chunks;
       const uint32_t q = tile - (uint32_t)args.split_base;
-      f32x4 *slot = reinterpret_cast<f32x4 *>(args.ws) + (size_t)(unit - (uint32_t)args.split_base) * (BM * BN / 4);
+      f32x4 *slot = reinterpret_cast<f32x4 *>(args.ws) + (size_t)(item - (uint32_t)args.split_base) * (BM * BN / 4);
 #pragma unroll
       for (int mi = 0; mi < CF::MI; ++mi)
 #pragma unroll
@@ -552,7 +558,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // ---- publish the next claim (producer) and log the tile
     if (wave == 0) {
       if constexpr (MODE == kDynamic) {
-        if (args.claims_ahead == 0 && !failed) {
+        if (args.claims_ahead == 0 && !failed && last_sub) {
           batch_ord = next_ord;
           batch[0] = claim_issue(args, region, lane);
           batch_n = 1;
@@ -569,9 +575,11 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     if (tid == 0) {
       const uint64_t t1 = clock_core();
       const uint64_t r1 = clock_wall();
-      if ((int32_t)unit < args.log_cap) {
+      if ((int32_t)item < args.log_cap) {
         TileRecDev rec;
         rec.tile = tile;
+        rec.unit = unit;
+        rec.pad = 0;
         rec.kb = (uint32_t)kb;
         rec.ke = (uint32_t)ke;
         rec.worker = blockIdx.x;
@@ -581,12 +589,17 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         rec.t1 = t1;
         rec.r0 = r0;
         rec.r1 = r1;
-        args.log[unit] = rec;
-        __hip_atomic_fetch_add(&args.visits[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        args.log[item] = rec;
+        __hip_atomic_fetch_add(&args.visits[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
 
-    // ---- advance
+    // ---- advance: the next item of this unit, else the next unit
+    if (!last_sub) {
+      ++sub;
+      continue;
+    }
+    sub = 0;
     if constexpr (MODE == kDynamic) {
       __syncthreads();
       const RingRec rec = ring[(ord + 1) % (uint32_t)args.ring_depth];

@@ -38,23 +38,27 @@ static_assert(sizeof(SchedCtrl) == 64, "control block layout");
 // arrival counter in the scheduler-state set.
 static constexpr int kMaxSplitTiles = 1024;
 
-// Work-unit log record as written by the kernel (unit-indexed). kb / ke: the
-// unit's k-steps [kb, ke) of BK each.
+// Log record as written by the kernel, one per work item (a whole tile or one
+// K-chunk of a split tile), indexed by item id. unit: the claimed work unit that
+// covered the item (items are units unless claim groups are on); kb / ke: the
+// item's k-steps [kb, ke) of BK each.
 struct TileRecDev {
   uint32_t tile, worker, hw_id, xcc_id;
   uint64_t t0, t1, r0, r1;
-  uint32_t kb, ke;
+  uint32_t kb, ke, unit, pad;
 };
-static_assert(sizeof(TileRecDev) == 56, "tile record layout");
+static_assert(sizeof(TileRecDev) == 64, "tile record layout");
 
 struct KernelArgs {
   KernelProblem single;         // the problem when G == 1 and !grouped
   const KernelProblem *groups;  // device array (grouped launches)
   int32_t G;
-  int32_t T;                    // total work units (tiles, plus the K-chunks of split tiles)
-  int32_t split_base;           // units >= split_base are K-chunks of the tiles split_base, ...; == T: no split
+  int32_t T;                    // work units handed out (claims, static steps, non-persistent blocks)
+  int32_t items;                // work items: tiles, plus the K-chunks of split tiles
+  int32_t claim_group;          // items per unit (1 unless claim groups are on; then nothing is split)
+  int32_t split_base;           // items >= split_base are K-chunks of the tiles split_base, ...; == items: no split
   int32_t split_chunks;         // K-chunks per split tile (S)
-  float *ws;                    // split partial sums: one BM x BN fp32 slot per K-chunk unit
+  float *ws;                    // split partial sums: one BM x BN fp32 slot per K-chunk item
   uint32_t *arrivals;           // this run's per-split-tile arrival counters (kMaxSplitTiles)
   int32_t P;                    // static stride (grid size of a static run)
   int32_t claims_ahead;         // 0, 1 or 2 (< ring_depth)
@@ -64,7 +68,7 @@ struct KernelArgs {
   int32_t raster_group;         // <= 1: row-major
   uint32_t counter_base;        // added to every claim (failure forcing)
   int32_t max_concurrent;       // 0: no gate
-  int32_t log_cap;              // units logged (0: none)
+  int32_t log_cap;              // items logged (0: none)
   SchedCtrl *ctrl;              // this run's set
   TileRecDev *log;
   uint32_t *visits;

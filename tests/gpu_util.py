@@ -66,20 +66,38 @@ def assert_close_rows(problem, c_gpu, rows):
     return rep
 
 
-def check_log(plan, mode, T, P=None, expected_tiles=None, K=None, tiles=None):
-    """Check the last run's log: T work units (== tiles unless the tail was split),
-    the per-mode ownership rules on unit ids, and, given K, that the units of each
-    of the `tiles` output tiles (default T) cover [0, K) exactly once."""
+def check_log(plan, mode, T, P=None, expected_tiles=None, K=None, tiles=None, group=1):
+    """Check the last run's log: T work items (== tiles unless the tail was split),
+    the per-mode ownership rules on work-unit ids (unit u covers items [u*group,
+    u*group + group): claim groups), and, given K, that the items of each of the
+    `tiles` output tiles (default T) cover [0, K) exactly once."""
     log = ptg.gemm_read_log(plan)
     assert len(log) == T, (len(log), T)
-    assert np.array_equal(log["unit"], np.arange(T))
-    ran = log[log["visits"] > 0]
+    assert np.array_equal(log["unit"], np.arange(T) // group)
     regions = 8 if int(getattr(plan.desc, "claim_policy", 0)) == 1 else 1
-    errs = check_ownership(mode, T, ran["unit"], ran["worker"], ran["r0"].astype(np.float64),
-                           ran["r1"].astype(np.float64), log["visits"], P=P, expected_tiles=expected_tiles,
-                           regions=regions)
-    assert not errs, errs
+    if group == 1:
+        ran = log[log["visits"] > 0]
+        errs = check_ownership(mode, T, ran["unit"], ran["worker"], ran["r0"].astype(np.float64),
+                               ran["r1"].astype(np.float64), log["visits"], P=P, expected_tiles=expected_tiles,
+                               regions=regions)
+        assert not errs, errs
+    else:
+        # every item once; a unit's items run on one worker, back to back, in item order
+        assert np.all(log["visits"] == 1), log["visits"]
+        U = -(-T // group)
+        worker = np.zeros(U, dtype=np.int64)
+        start = np.zeros(U)
+        end = np.zeros(U)
+        for u in range(U):
+            it = log[u * group:(u + 1) * group]
+            assert len(np.unique(it["worker"])) == 1, (u, it["worker"])
+            assert np.all(it["r0"][1:] >= it["r1"][:-1]), u
+            worker[u], start[u], end[u] = it["worker"][0], it["r0"][0], it["r1"][-1]
+        errs = check_ownership(mode, U, np.arange(U), worker, start, end, np.ones(U, dtype=np.int64), P=P,
+                               regions=regions)
+        assert not errs, errs
     if K is not None:
+        ran = log[log["visits"] > 0]
         errs = check_k_cover(ran["tile"], ran["k_begin"], ran["k_end"], T if tiles is None else tiles, K)
         assert not errs, errs
     return log

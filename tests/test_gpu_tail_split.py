@@ -57,7 +57,7 @@ def test_tail_split_full_wave_plus_tail(shape):
         say(f"case tail split shape={shape} mode={mode}")
         c = run(p, plan, mode)
         info = ptg.gemm_plan_info_get(plan)
-        U = info["last_units"]
+        U = info["last_items"]
         assert info["last_tiles"] == T and info["last_split_chunks"] >= 2, info
         log = check_log(plan, mode, U, P=info["last_grid"] if mode == "static" else None, K=K, tiles=T)
         want = _expect_units(plan, log, T, workers, K, 8)
@@ -82,8 +82,8 @@ def test_tail_split_static_few_workers_ragged():
     c = run(p, plan, "static")
     info = ptg.gemm_plan_info_get(plan)
     T = 3 * 4
-    assert info["last_units"] == 10 + 2 * 2
-    log = check_log(plan, "static", info["last_units"], P=5, K=K, tiles=T)
+    assert info["last_items"] == info["last_units"] == 10 + 2 * 2
+    log = check_log(plan, "static", info["last_items"], P=5, K=K, tiles=T)
     _expect_units(plan, log, T, 5, K, 8)
     for w in range(5):
         assert sorted(log["unit"][log["worker"] == w].tolist()) == list(range(w, 14, 5))
@@ -99,7 +99,8 @@ def test_tail_split_falls_back_to_whole_tiles():
     say("case tail split fallback")
     c = run(p, plan, "dynamic")
     info = ptg.gemm_plan_info_get(plan)
-    assert info["last_units"] == info["last_tiles"] == 257 and info["last_split_chunks"] == 1
+    assert info["last_items"] == info["last_units"] == info["last_tiles"] == 257
+    assert info["last_split_chunks"] == 1
     check_log(plan, "dynamic", 257, K=K)
     assert_close_rows(p, c, [0, 5, M // 2, M - 1])
     plan.destroy()
