@@ -268,6 +268,10 @@ def main():
     ap.add_argument("--no-modes", action="store_true", help="skip timing the other schedulers")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) to scale the HBM byte counters")
+    ap.add_argument("--profile-workload", default="", metavar="NAME",
+                    choices=["", "tail_255", "tail_256", "tail_257"],
+                    help="only run that single-GEMM workload (--steps times, after --warmup) for a profiler; "
+                         "prints its timing and algorithmic HBM rate, not the benchmark line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -276,6 +280,25 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.profile_workload:
+        import persistent_tiled_gemm_amd as ptg
+        from workloads import make_workload
+        ptg.load_library()
+        q = make_workload(args.profile_workload).problems[0]
+        A = ptg.bf16_from_bits(q.a_bits)
+        B = ptg.bf16_from_bits(q.b_bits)
+        C = torch.empty((q.M, q.N), dtype=torch.float32, device="cuda")
+        plan = ptg.gemm_create(tile_edge=256, claim_policy=args.claim_policy, log_capacity=0 if args.no_log else 512)
+        stream = torch.cuda.current_stream()
+        ms = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=args.mode, stream=stream), args.steps, args.warmup,
+                       stream)
+        nbytes = q.M * q.K * 2 + q.K * q.N * 2 + q.M * q.N * 4
+        print(json.dumps({"workload": args.profile_workload, "mode": args.mode, "ms": ms,
+                          "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / (ms * 1e-3) / 1e9,
+                          "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "tflops": 2.0 * q.M * q.N * q.K / (ms * 1e-3) / 1e12}), flush=True)
+        plan.destroy()
+        return
     if args.calibrate_copy > 0:
         n = args.calibrate_copy * (1 << 20)
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")

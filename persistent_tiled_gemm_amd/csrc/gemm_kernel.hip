@@ -1,10 +1,12 @@
 // Persistent tiled bf16 GEMM for gfx950: C (fp32) = A (bf16, M x K) . B (bf16, K x N).
 //
-// One workgroup = a grid of wave64s (2 x 2 for 128 x 128 tiles, 2 x 4 for
-// 256 x 256 tiles, i.e. two waves per SIMD); each wave owns a block of the
-// output tile and accumulates it in fp32 with v_mfma_f32_32x32x16_bf16. Operand tiles move global -> LDS with
-// buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR round trip) into two
-// LDS stages, so the loads of k-step kt+1 overlap the MFMAs of k-step kt.
+// One workgroup = a grid of wave64s (2 x 2 for 128 x 128 tiles, two workgroups
+// per CU; 2 x 4 for 256 x 256 tiles, one workgroup per CU); either way two
+// waves share each SIMD. Each wave owns a block of the output tile and
+// accumulates it in fp32 with v_mfma_f32_32x32x16_bf16. Operand tiles move
+// global -> LDS with buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR
+// round trip) into two LDS stages, so the loads of k-step kt+1 overlap the
+// MFMAs of k-step kt.
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so fragment reads are bank-conflict
 // free):
@@ -19,6 +21,13 @@
 // The MFMA is issued with the B fragment as its first operand, so the
 // accumulator of lane l holds four consecutive n of row m = l % 32, which the
 // epilogue writes as one 16-byte store.
+//
+// Work units. The schedulers hand out work units; a unit is one work item, or
+// with claim groups g consecutive items that one worker runs back to back. An
+// item is a whole tile, or with a split tail one K-chunk of a tile of the
+// partial last wave: a chunk stores its fp32 partial tile to plan scratch and
+// the workgroup that completes the tile's last chunk adds the partials in chunk
+// order and writes C (no workgroup ever waits for another).
 //
 // Scheduling: see the header comment of ptg_gemm.h. The work loop is the
 // persistent worker loop of the blog post "CUTLASS Cluster Launch Control
