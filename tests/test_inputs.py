@@ -48,3 +48,17 @@ def test_grouped_k_values_and_small_workloads():
     assert w.tile == 128 and w.problems[0].a_bits.shape == (384, 512) and w.problems[0].b_bits.shape == (512, 512)
     g = make_workload("grouped_uneven", groups=4)
     assert [p.K for p in g.problems] == grouped_k_values(0, groups=4).tolist()
+
+
+def test_bf16_rounding_every_high_half_and_rounding_class():
+    # the result depends only on the high 16 bits and on where the low 16 bits sit
+    # against the halfway point 0x8000 (below, at, above); every high half is paired
+    # with the low halves at and around those boundaries (NaN patterns excluded)
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    u = (hi[:, None] | lows[None, :]).ravel()
+    x = u.view(np.float32)
+    x = x[~np.isnan(x)]
+    ours = f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
