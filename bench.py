@@ -377,6 +377,12 @@ def main():
            "frac_peak": tflops / PEAK_BF16_TFLOPS, "roofline": roof,
            "modes": modes}
 
+    # context for the roofline: the MFMA-only rate and clock with random operands (no memory traffic),
+    # the ceiling the power limit leaves any bf16 GEMM on this part
+    if not args.no_modes:
+        ptg.gemm_mfma_probe(iters=40000, random_operands=True)  # warm-up: the clock settles
+        out["mfma_ceiling"] = dict(ptg.gemm_mfma_probe(iters=40000, random_operands=True),
+                                   what="MFMA-only kernel, random bf16 operands, all CUs, second of two runs")
     if not args.no_tail:
         out["tail"] = run_tail_sections(ptg, torch, stream, khz, (p, A, B, C))
     plan.destroy()

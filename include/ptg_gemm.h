@@ -271,6 +271,20 @@ gemm_status gemm_test_preset_counter(gemm_tile_cfg tile_cfg, uint32_t start);
 gemm_status gemm_spoiler_run(int32_t device, int32_t n_wgs, int64_t spin_ns, void *stream,
                              uint64_t *d_log, double wait_resident_ms);
 
+/*
+ * Measurement helper (no page behind it; a fact about the part): run an
+ * MFMA-only kernel on `device`, one workgroup of four waves per CU, each wave
+ * issuing `iters` rounds of eight independent v_mfma_f32_32x32x16_bf16 with no
+ * memory traffic, operands constant (random_operands == 0) or changing from
+ * one MFMA to the next (pseudo-random bf16). Synchronous: it allocates a small
+ * scratch buffer, times the launch with events and frees the buffer. Outputs:
+ * *tflops_out, the dense bf16 rate achieved, and *clock_ghz_out, the mean
+ * shader clock during the run (s_memtime over s_memrealtime ticks). iters must
+ * be in 1..10^7.
+ */
+gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operands, double *tflops_out,
+                            double *clock_ghz_out);
+
 #ifdef __cplusplus
 }
 #endif

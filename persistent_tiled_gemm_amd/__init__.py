@@ -36,7 +36,7 @@ STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_E_INVALID_ARG", -2: "GEMM_E_SHAPE", -3: 
 # exported names, in the order of the header
 ABI_FUNCTIONS = ("gemm_default_desc", "gemm_create", "gemm_run", "gemm_run_grouped", "gemm_read_log",
                  "gemm_plan_info_get", "gemm_destroy", "gemm_status_str", "gemm_last_hip_error",
-                 "gemm_test_preset_counter", "gemm_spoiler_run")
+                 "gemm_test_preset_counter", "gemm_spoiler_run", "gemm_mfma_probe")
 
 
 class PtgError(RuntimeError):
@@ -105,6 +105,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gemm_last_hip_error.restype = ctypes.c_char_p
     lib.gemm_test_preset_counter.argtypes = [vp, u32]
     lib.gemm_spoiler_run.argtypes = [i32, i32, i64, vp, vp, ctypes.c_double]
+    lib.gemm_mfma_probe.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     for name in ABI_FUNCTIONS:
         if name not in ("gemm_status_str", "gemm_last_hip_error"):
             getattr(lib, name).restype = ctypes.c_int32
@@ -291,6 +292,16 @@ def gemm_spoiler_run(n_wgs: int, spin_ns: int, stream=None, log=None, wait_resid
     st = load_library().gemm_spoiler_run(int(device), int(n_wgs), int(spin_ns), ctypes.c_void_p(_stream_ptr(stream)),
                                          log_ptr, float(wait_resident_ms))
     _check(st, "gemm_spoiler_run")
+
+
+def gemm_mfma_probe(iters: int = 20000, random_operands: bool = True, device: int = 0) -> dict:
+    """gemm_mfma_probe: MFMA-only bf16 rate and shader clock on every CU (no memory traffic)."""
+    tf = ctypes.c_double(0.0)
+    ghz = ctypes.c_double(0.0)
+    st = load_library().gemm_mfma_probe(int(device), int(iters), 1 if random_operands else 0, ctypes.byref(tf),
+                                        ctypes.byref(ghz))
+    _check(st, "gemm_mfma_probe")
+    return {"tflops": tf.value, "clock_ghz": ghz.value}
 
 
 def bf16_from_bits(bits: np.ndarray, device="cuda"):

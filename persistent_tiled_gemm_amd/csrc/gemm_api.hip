@@ -591,4 +591,52 @@ gemm_status gemm_spoiler_run(int32_t device, int32_t n_wgs, int64_t spin_ns, voi
   return GEMM_OK;
 }
 
+gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operands, double *tflops_out,
+                            double *clock_ghz_out) {
+  if (!tflops_out || !clock_ghz_out || iters < 1 || iters > 10000000) return GEMM_E_INVALID_ARG;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GEMM_E_HIP;
+  if (cur != device) return GEMM_E_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return GEMM_E_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_E_UNSUPPORTED;
+  const int grid = prop.multiProcessorCount;
+  float *sink = nullptr;
+  uint64_t *ticks = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  gemm_status st = GEMM_OK;
+  std::vector<uint64_t> h((size_t)grid * 2);
+  float ms = 0.0f;
+  if (hipMalloc(&sink, sizeof(float) * 256 * (size_t)grid) != hipSuccess ||
+      hipMalloc(&ticks, sizeof(uint64_t) * 2 * (size_t)grid) != hipSuccess) {
+    st = GEMM_E_NOMEM;
+  } else if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess ||
+             hipEventRecord(e0, nullptr) != hipSuccess ||
+             ptg::launch_mfma_probe(grid, iters, random_operands != 0, sink, ticks, nullptr) != hipSuccess ||
+             hipEventRecord(e1, nullptr) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+             hipEventElapsedTime(&ms, e0, e1) != hipSuccess ||
+             hipMemcpy(h.data(), ticks, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost) != hipSuccess) {
+    st = GEMM_E_HIP;
+  }
+  if (st == GEMM_OK) {
+    int wclk = 0;
+    if (hipDeviceGetAttribute(&wclk, hipDeviceAttributeWallClockRate, device) != hipSuccess || wclk <= 0) {
+      st = GEMM_E_HIP;
+    } else {
+      double ratio = 0.0;
+      for (int i = 0; i < grid; ++i) ratio += (double)h[2 * i] / (double)std::max<uint64_t>(h[2 * i + 1], 1);
+      ratio /= grid;
+      // 4 waves x 8 MFMAs x 32*32*16*2 flop per round and workgroup
+      const double flops = 4.0 * 8.0 * 32768.0 * (double)iters * (double)grid;
+      *tflops_out = flops / ((double)ms * 1e-3) / 1e12;
+      *clock_ghz_out = ratio * (double)wclk * 1e-6;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (sink) (void)hipFree(sink);
+  if (ticks) (void)hipFree(ticks);
+  return st;
+}
+
 }  // extern "C"
