@@ -7,7 +7,7 @@ fallback; if the library is missing, loading it raises.
 The function names are the C ABI's: gemm_default_desc, gemm_create, gemm_run,
 gemm_run_grouped, gemm_read_log, gemm_plan_info_get, gemm_destroy,
 gemm_status_str, gemm_last_hip_error, gemm_test_preset_counter,
-gemm_spoiler_run. Tensors are torch device tensors: A and B bf16 (or int16 /
+gemm_spoiler_run, gemm_mfma_probe. Tensors are torch device tensors: A and B bf16 (or int16 /
 uint16 views of bf16 bits), C float32, all contiguous; streams are
 torch.cuda streams (default: the current stream).
 """
@@ -88,6 +88,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise OSError(f"{p} is missing: build it with `python -m persistent_tiled_gemm_amd.build`")
+    # torch brings its own HIP runtime with the same soname as the system one the
+    # library is linked against; whichever loads first serves the whole process.
+    # Importing torch first makes that torch's, so the library and the caller's
+    # tensors and streams share one runtime (the other order leaves torch unable
+    # to see the GPU).
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - the library is still usable from C
+        pass
     lib = ctypes.CDLL(p)
     vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
     P64 = ctypes.POINTER(ctypes.c_int64)

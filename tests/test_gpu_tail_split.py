@@ -121,3 +121,23 @@ def test_split_result_close_to_whole_tiles():
     assert np.array_equal(ca[: 256 * 256], cb[: 256 * 256])  # whole tiles: identical code and k order
     a.destroy()
     b.destroy()
+
+
+@pytest.mark.parametrize("tile,q,policy", [(256, 0, 1), (256, 2, 0), (128, 1, 1), (128, 2, 1)])
+def test_tail_split_with_claim_options(tile, q, policy):
+    # the split tail under other claim settings and the 128 tile: T = workers + 3 tiles
+    torch = __import__("torch")
+    plan = make_plan(tile, tail_split=4, claims_ahead=q, claim_policy=policy, log_capacity=4096)
+    info = ptg.gemm_plan_info_get(plan)
+    workers = info["occupancy"] * info["cu_count"]
+    T = workers + 3
+    M, N, K = T * tile, tile, 512 + 40
+    p = make_problem(M, N, K, "uniform", seed=tile + q)
+    say(f"case tail split tile={tile} claims_ahead={q} policy={policy} T={T}")
+    c = run(p, plan, "dynamic")
+    info = ptg.gemm_plan_info_get(plan)
+    log = check_log(plan, "dynamic", info["last_items"], K=K, tiles=T)
+    want = _expect_units(plan, log, T, workers, K, 4)
+    rows = _split_rows(want, tile, M, 1) + [0, tile, M // 2]
+    assert_close_rows(p, c, rows)
+    plan.destroy()
