@@ -250,9 +250,9 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // ---- the work item: unit u covers items [u g, u g + g) (g = claim_group, 1
     // unless claim groups are on); items below split_base are whole tiles (id =
     // tile id), item split_base + q*S + c is K-chunk c of tile split_base + q
-    const uint32_t g = (uint32_t)args.claim_group;
-    const uint32_t item = unit * g + sub;
-    const bool last_sub = sub + 1 >= min(g, (uint32_t)args.items - unit * g);
+    const uint32_t group = (uint32_t)args.claim_group;
+    const uint32_t item = unit * group + sub;
+    const bool last_sub = sub + 1 >= min(group, (uint32_t)args.items - unit * group);
     uint32_t tile = item;
     uint32_t chunk = 0;
     const bool split = !GROUPED && (int32_t)item >= args.split_base;
@@ -264,8 +264,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     KernelProblem pb;
     int32_t local = (int32_t)tile;
     if constexpr (GROUPED) {
-      const int32_t g = find_problem(args.groups, args.G, (int32_t)tile);
-      pb = args.groups[g];
+      const int32_t prob = find_problem(args.groups, args.G, (int32_t)tile);
+      pb = args.groups[prob];
       // the descriptor is the same for the whole workgroup: keep it in SGPRs
       pb.A = uniform_ptr(pb.A);
       pb.B = uniform_ptr(pb.B);
