@@ -2,7 +2,7 @@
 """Benchmark: bf16 GEMM TFLOP/s and % of MFMA peak on 8192^3; tail makespans.
 
 One step = one pass of the whole hot path: a gemm_run of the dynamic scheduler
-(atomic claim counter + LDS claim ring) on M = N = K = 8192, 256x256x64 tiles,
+(atomic claim counter + LDS claim ring) on M = N = K = 8192, 256x256 tiles (K staged 32 deep),
 A and B i.i.d. N(0,1)/sqrt(K) in bf16, fp32 C, tile log on. Inputs are resident
 in HBM before timing starts. The kernel time is measured with HIP events on
 the stream the kernel is launched on.
@@ -369,7 +369,7 @@ def main():
     out = {"metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "square_8192", "M": M, "N": N, "K": K, "tile": [256, 256, 64],
+           "config": {"workload": "square_8192", "M": M, "N": N, "K": K, "tile": [256, 256, 32],
                       "sched": args.mode, "claim_policy": "xcd_counters" if args.claim_policy == 1 else "single_counter",
                       "claims_ahead": args.claims_ahead, "ring_depth": 3,
                       "raster_group": args.raster_group, "tile_log": not args.no_log, "accumulate": "fp32",

@@ -91,14 +91,15 @@ typedef enum gemm_sched_mode {
 
 /*
  * Plan descriptor (a value type; gemm_create copies it). Fields:
- *   bm, bn, bk      output tile and K step: {128,128,64} or {256,256,64}.
+ *   bm, bn, bk      output tile and K step: {128,128,32} or {256,256,32}
+ *                   (the kernel stages 32-deep slices of K in a ring of four).
  *   ring_depth      depth of the LDS ring of claim records: 3 (2..3 accepted).
  *   claims_ahead    throttle: how many claims a dynamic worker holds beyond its
  *                   current tile: 0 (claim after finishing the tile), 1 or 2;
  *                   must be < ring_depth.
  *   claim_lead      with claims_ahead >= 1, the claims for later tiles are issued
  *                   at the start of k-step max(0, nk - claim_lead) of the current
- *                   tile (nk = its number of 64-deep k-steps): late, so a worker
+ *                   tile (nk = its number of 32-deep k-steps): late, so a worker
  *                   does not take work a not-yet-started slot would get, yet
  *                   early enough for the atomic's round trip to hide under the
  *                   MFMAs. 0 = at the last k-step; >= nk = at the tile start.

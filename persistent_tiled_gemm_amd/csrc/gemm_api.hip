@@ -71,7 +71,7 @@ gemm_status hip_fail(gemm_plan *p, hipError_t e, const char *what) {
 }
 
 bool valid_tile(const gemm_tile_desc &d) {
-  return (d.bm == 256 && d.bn == 256 && d.bk == 64) || (d.bm == 128 && d.bn == 128 && d.bk == 64);
+  return (d.bm == 256 && d.bn == 256 && d.bk == 32) || (d.bm == 128 && d.bn == 128 && d.bk == 32);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -100,8 +100,8 @@ unsigned char *ctrl_set(gemm_plan *p, uint64_t run) { return p->d_ctrl_block + (
 constexpr size_t kArrivalsOffset = sizeof(SchedCtrl);
 constexpr size_t kVisitsOffset = sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)ptg::kMaxSplitTiles;
 
-// Fewest k-steps a K-chunk of a split tile gets.
-constexpr int64_t kMinChunkSteps = 4;
+// Fewest k-steps (of bk = 32) a K-chunk of a split tile gets.
+constexpr int64_t kMinChunkSteps = 8;
 
 // Work items of a run: T whole tiles, or, with tail splitting on, the tiles
 // that fill whole waves of `workers` plus the r = T mod workers tiles of the
@@ -195,7 +195,7 @@ const char *gemm_status_str(int32_t status) {
     case GEMM_OK: return "ok";
     case GEMM_E_INVALID_ARG: return "invalid argument";
     case GEMM_E_SHAPE: return "unsupported shape (negative, K or N not a multiple of 8, or over a size limit)";
-    case GEMM_E_UNSUPPORTED: return "unsupported device or tile configuration (gfx950 only; tiles 128x128x64 or 256x256x64)";
+    case GEMM_E_UNSUPPORTED: return "unsupported device or tile configuration (gfx950 only; tiles 128x128x32 or 256x256x32)";
     case GEMM_E_DEVICE: return "plan used while a different device is current";
     case GEMM_E_HIP: return "HIP runtime error";
     case GEMM_E_NOMEM: return "out of memory";
@@ -210,10 +210,10 @@ gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t de
   if (tile_edge != 128 && tile_edge != 256) return GEMM_E_UNSUPPORTED;
   std::memset(out, 0, sizeof(*out));
   out->bm = out->bn = tile_edge;
-  out->bk = 64;
+  out->bk = 32;
   out->ring_depth = 3;
   out->claims_ahead = 1;
-  out->claim_lead = 2;
+  out->claim_lead = 4;
   out->claim_policy = 1;
   out->raster = 0;
   out->raster_group = 8;

@@ -5,15 +5,15 @@
 // waves share each SIMD. Each wave owns a block of the output tile and
 // accumulates it in fp32 with v_mfma_f32_32x32x16_bf16. Operand tiles move
 // global -> LDS with buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR
-// round trip) into two LDS stages, so the loads of k-step kt+1 overlap the
-// MFMAs of k-step kt.
+// round trip) into a ring of four 32-deep LDS stages: the loads of k-step kt+3
+// go out during k-step kt, so each load has three k-steps to land.
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so fragment reads are bank-conflict
 // free):
-//   A stage: BM rows x 64 k, 128 B per row; logical chunk c of row r sits in slot
-//            c ^ ((r ^ (r >> 3)) & 7). A fragments are read with ds_read_b128
+//   A stage: BM rows x 32 k, 64 B per row; logical chunk c of row r sits in slot
+//            c ^ ((r >> 2) & 3). A fragments are read with ds_read_b128
 //            (8 consecutive k of one row per lane).
-//   B stage: 64 k rows x BN n; logical chunk c of row k sits in slot
+//   B stage: 32 k rows x BN n; logical chunk c of row k sits in slot
 //            c ^ (10 (k & 1) + 4 ((k >> 1) & 1)). B fragments need 8 consecutive
 //            k of one column per lane; ds_read_b64_tr_b16 delivers them from the
 //            row-major (n-contiguous) tile: in each 16-lane group, lane L reads 4
@@ -48,7 +48,10 @@ struct Cfg {
   static constexpr int BM_ = BM, BN_ = BN, WAVES_N_ = WAVES_N;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * NW;
-  static constexpr int BK = 64;
+  static constexpr int BK = 32, NSTAGE = 4;          // k per stage, LDS stages
+  static constexpr int A_ROW = BK * 2;              // bytes per row of the A stage
+  static constexpr int A_ROW_CHUNKS = BK / 8;
+  static constexpr int A_RPL = 1024 / A_ROW;         // A rows one wave-load (64 x 16 B) covers
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
   static constexpr int MI = WM / 32, NI = WN / 32;            // 32x32 MFMA blocks per wave
   static constexpr int A_LOADS = BM * (BK / 8) / THREADS;     // 16-byte loads per thread per stage
@@ -58,7 +61,7 @@ struct Cfg {
   static constexpr int B_ROW = BN * 2;              // bytes per k row of the B stage
   static constexpr int B_ROW_CHUNKS = BN / 8;
   static constexpr int STAGE = A_STAGE + B_STAGE;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = NSTAGE * STAGE;
   static_assert(A_LOADS * THREADS == BM * (BK / 8) && B_LOADS * THREADS == BK * (BN / 8), "load split");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
 };
@@ -77,7 +80,7 @@ template <> struct TileCfg<256> { using type = Cfg<256, 256, 2, 4>; };
 template <> struct TileCfg<256> { using type = Cfg<256, 256, 2, 2>; };
 #endif
 
-__device__ __forceinline__ uint32_t swz_a(uint32_t row) { return (row ^ (row >> 3)) & 7u; }
+__device__ __forceinline__ uint32_t swz_a(uint32_t row) { return (row >> 2) & 3u; }
 __device__ __forceinline__ uint32_t swz_b(uint32_t k) { return 10u * (k & 1u) + 4u * ((k >> 1) & 1u); }
 
 // One record of the claim ring: the answer to one claim. `valid` is the success
@@ -171,7 +174,7 @@ template <int BM, int BN, int MODE, bool GROUPED>
 __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel(const KernelArgs args) {
   using CF = typename TileCfg<BM>::type;
   static_assert(CF::BM_ == BM && CF::BN_ == BN, "config");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::LDS];  // two stages
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[CF::LDS];  // the stage ring
   __shared__ RingRec ring[kRingDepth];
   __shared__ uint32_t gate_ok;
   __shared__ uint32_t split_last;  // this workgroup finished the last K-chunk of a split tile
@@ -314,8 +317,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // per-load voffset is one of two (A) or one (B) per-lane bases plus a
     // wave-uniform step.
     constexpr uint32_t kBRowsPerLoad = 64u / CF::B_ROW_CHUNKS;  // k rows one wave-load covers
-    const uint32_t a_row0 = wave * 8u + (lane >> 3);             // row of load j = a_row0 + 8 NW j
-    const uint32_t a_c0 = ((lane & 7u) ^ (lane >> 3) ^ wave) & 7u;  // chunk of load j = a_c0 ^ ((j NW) & 7)
+    const uint32_t a_row0 = wave * (uint32_t)CF::A_RPL + lane / CF::A_ROW_CHUNKS;  // row of load j = a_row0 + RPL NW j
+    const uint32_t a_c0 = (lane % CF::A_ROW_CHUNKS) ^ swz_a(a_row0);
     const uint32_t a_base = a_row0 * (uint32_t)K * 2u;
     const uint32_t b_k0 = wave * kBRowsPerLoad + lane / CF::B_ROW_CHUNKS;  // k row of load j = b_k0 + NW*kBRowsPerLoad j
     const uint32_t b_c = (lane % CF::B_ROW_CHUNKS) ^ swz_b(b_k0);
@@ -336,9 +339,10 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       const int32_t k0 = kt * CF::BK;
       const bool tail = kt >= full;
       if (j < CF::A_LOADS) {
-        const uint32_t row = a_row0 + 8u * CF::NW * (uint32_t)j;
-        const uint32_t c = a_c0 ^ (uint32_t)((j * CF::NW) & 7);
-        const uint32_t vo = a_base + c * 16u + (uint32_t)j * 16u * CF::NW * (uint32_t)K;
+        const uint32_t row = a_row0 + (uint32_t)(CF::A_RPL * CF::NW) * (uint32_t)j;
+        // the swizzle of load j's row differs from a_row0's by a compile-time XOR
+        const uint32_t c = a_c0 ^ (swz_a((uint32_t)(CF::A_RPL * CF::NW * j)) ^ swz_a(0u));
+        const uint32_t vo = a_base + c * 16u + (uint32_t)(CF::A_RPL * CF::NW * j) * (uint32_t)K * 2u;
         const bool out = (int32_t)row >= m_left || (tail && k0 + (int32_t)(c * 8u) >= K);
         return out ? kBufOob : vo;
       }
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 #pragma unroll
     for (int mi = 0; mi < CF::MI; ++mi) {
       const uint32_t row = wm * CF::WM + mi * 32 + (lane & 31u);
-      off_a[mi] = row * 128u;
+      off_a[mi] = row * (uint32_t)CF::A_ROW;
       swa[mi] = swz_a(row) ^ (lane >> 5);
     }
     uint32_t off_b[CF::NI];
@@ -457,37 +461,32 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     if (ke == kb && last_sub) do_claims();
 
     if (ke > kb) {
+      // four 32-deep stages: the loads of k-step kt+3 go out during k-step kt
+      // into the stage k-step kt-1 just left, so a load has three k-steps to land
       constexpr int kLoads = CF::A_LOADS + CF::B_LOADS;
       constexpr int kReads = CF::MI + 2 * CF::NI;
       constexpr int kMfma = CF::MI * CF::NI;
+      static_assert(CF::NSTAGE == 4 && kLoads == 4, "stage ring");
       issue_all(0, kb);
-      wait_vmem_all();
+      issue_all(1, kb + 1 < ke ? kb + 1 : ke - 1);
+      issue_all(2, kb + 2 < ke ? kb + 2 : ke - 1);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       wg_barrier();
       bf16x8 a0[CF::MI], b0[CF::NI], a1[CF::MI], b1[CF::NI];
       read_frags(0, 0, a0, b0, 0, 0, 0, 0);
       for (int32_t kt = kb; kt < ke; ++kt) {
-        // k-step kt on stage st while k-step kt+1 streams into stage st^1 (the
-        // last k-step reloads its own data instead, so no load is out of range);
-        // the loads are spread over the first two k-slices, between MFMAs
-        const int st = (kt - kb) & 1;
+        const int st = (kt - kb) & 3;
         if (kt == claim_at) do_claims();
-        const int32_t kl = kt + 1 < ke ? kt + 1 : kt;
-        read_frags(st, 1, a1, b1, st ^ 1, kl, 0, kLoads / 2);
+        const int32_t kl = kt + 3 < ke ? kt + 3 : ke - 1;
+        read_frags(st, 1, a1, b1, (st + 3) & 3, kl, 0, kLoads);
         mma(a0, b0);
         interleave<kReads, kMfma>();
-        read_frags(st, 2, a0, b0, st ^ 1, kl, kLoads / 2, kLoads - kLoads / 2);
-        mma(a1, b1);
-        interleave<kReads, kMfma>();
-        read_frags(st, 3, a1, b1, 0, 0, 0, 0);
-        mma(a0, b0);
-        interleave<kReads, kMfma>();
-        // stage st fully read and stage st^1 landed: publish it to every wave
+        // stage st fully read and stage st+1 landed (its loads went out two k-steps
+        // ago; the eight loads issued since may still be in flight)
         wait_lds_all();
-        wait_vmem_all();
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         wg_barrier();
-        // slice 3 runs while slice 0 of the next stage is read (after the last
-        // k-step these values are never used)
-        read_frags(st ^ 1, 0, a0, b0, 0, 0, 0, 0);
+        read_frags((st + 1) & 3, 0, a0, b0, 0, 0, 0, 0);
         mma(a1, b1);
         interleave<kReads, kMfma>();
       }

@@ -49,7 +49,7 @@ def test_status_strings_and_defaults(lib):
         assert ptg.gemm_status_str(s) not in ("", "unknown status")
     assert ptg.gemm_status_str(-99) == "unknown status"
     d = ptg.gemm_default_desc(256, 0)
-    assert (d.bm, d.bn, d.bk, d.ring_depth, d.claims_ahead, d.claim_lead, d.claim_policy) == (256, 256, 64, 3, 1, 2, 1)
+    assert (d.bm, d.bn, d.bk, d.ring_depth, d.claims_ahead, d.claim_lead, d.claim_policy) == (256, 256, 32, 3, 1, 4, 1)
     d = ptg.gemm_default_desc(128, 0)
     assert (d.bm, d.bn) == (128, 128)
     with pytest.raises(ptg.PtgError):

@@ -104,8 +104,8 @@ def test_tail_split_shortens_the_partial_wave():
         torch.cuda.synchronize()
         res[name] = _span(ptg.gemm_read_log(plan), khz)
     t = res["whole"][1]
-    nk = q.K // 64
-    units = split_units(257, 256, nk, 4)
+    nk = q.K // 32
+    units = split_units(257, 256, nk, 4, min_chunk_steps=8)
     model_whole = simulate([1.0] * 257, "dynamic", slots=256).makespan
     model_split = simulate([(e - b) / nk for _, b, e in units], "dynamic", slots=256).makespan
     say(f"  whole {res['whole'][0] / t:.2f} t (model {model_whole}), split {res['split'][0] / t:.2f} t "

@@ -22,7 +22,7 @@ MODES = ("nonpersistent", "static", "dynamic")
 # shapes spanning several tiles with ragged tails in M, N and K
 SMALL_SHAPES = [
     (384, 512, 512),    # the twelve 128x128 tiles of the worked example
-    (256, 256, 64),     # one 256 tile, one k-step
+    (256, 256, 64),     # one 256 tile, two k-steps
     (1000, 776, 264),   # ragged M, N, K
     (513, 264, 72),
     (1, 8, 8),          # degenerate: one row, one k chunk
@@ -131,7 +131,7 @@ def test_plan_validation():
         with pytest.raises(ptg.PtgError):
             ptg.gemm_create(**bad)
     d = ptg.gemm_default_desc(256, 0)
-    d.bk = 32
+    d.bk = 64
     with pytest.raises(ptg.PtgError) as e:
         ptg.Plan(d)
     assert e.value.status == -3

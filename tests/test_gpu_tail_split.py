@@ -22,12 +22,12 @@ MODES = ("nonpersistent", "static", "dynamic")
 
 
 def _expect_units(plan, log, T, workers, K, max_chunks):
-    nk = -(-K // 64)
-    want = split_units(T, workers, nk, max_chunks)
+    nk = -(-K // 32)                       # 32-deep k-steps; chunks get at least 8 of them
+    want = split_units(T, workers, nk, max_chunks, min_chunk_steps=8)
     assert len(log) == len(want), (len(log), len(want))
     tiles = np.array([u[0] for u in want])
-    kb = np.minimum(np.array([u[1] for u in want]) * 64, K)
-    ke = np.minimum(np.array([u[2] for u in want]) * 64, K)
+    kb = np.minimum(np.array([u[1] for u in want]) * 32, K)
+    ke = np.minimum(np.array([u[2] for u in want]) * 32, K)
     assert np.array_equal(log["tile"], tiles)
     assert np.array_equal(log["k_begin"], kb) and np.array_equal(log["k_end"], ke)
     return want
@@ -74,7 +74,7 @@ def test_tail_split_full_wave_plus_tail(shape):
 
 def test_tail_split_static_few_workers_ragged():
     # P = 5 static workers, 12 tiles: 10 whole, the 2 tail tiles in 2 chunks each;
-    # K = 520 is not a multiple of 64 (the last chunk holds the K tail)
+    # K = 520 is not a multiple of 32 (the last chunk holds the K tail)
     M, N, K = 700, 1024, 520
     p = make_problem(M, N, K, "normal", seed=3)
     plan = make_plan(256, tail_split=8, static_workers=5)
@@ -92,7 +92,7 @@ def test_tail_split_static_few_workers_ragged():
 
 
 def test_tail_split_falls_back_to_whole_tiles():
-    # K = 192 is 3 k-steps: fewer than two chunks of 4, so nothing is split
+    # K = 192 is 6 k-steps of 32: fewer than two chunks of 8, so nothing is split
     M, N, K = 257 * 128, 128, 192
     p = make_problem(M, N, K, "uniform", seed=11)
     plan = make_plan(128, tail_split=8, min_lds_bytes=96 * 1024)
