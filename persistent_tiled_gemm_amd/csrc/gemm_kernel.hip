@@ -1,25 +1,27 @@
 // Persistent tiled bf16 GEMM for gfx950: C (fp32) = A (bf16, M x K) . B (bf16, K x N).
 //
-// One workgroup = a grid of wave64s (2 x 2 for 128 x 128 tiles, two workgroups
-// per CU; 2 x 4 for 256 x 256 tiles, one workgroup per CU); either way two
-// waves share each SIMD. Each wave owns a block of the output tile and
-// accumulates it in fp32 with v_mfma_f32_32x32x16_bf16. Operand tiles move
+// One workgroup = a 2 x 2 grid of wave64s. 256 x 256 tiles: one workgroup per
+// CU, each wave owns 128 x 128 of the tile as 8 x 8 blocks of
+// v_mfma_f32_16x16x32_bf16 (one wave per SIMD). 128 x 128 tiles: two
+// workgroups per CU, each wave owns 64 x 64 as 2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16. Accumulation is fp32 throughout. Operand tiles move
 // global -> LDS with buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR
-// round trip) into a ring of four 32-deep LDS stages: the loads of k-step kt+3
-// go out during k-step kt, so each load has three k-steps to land.
+// round trip) into a ring of four 32-deep LDS stages, each load two to three
+// k-steps ahead of its first reader.
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so fragment reads are bank-conflict
 // free):
 //   A stage: BM rows x 32 k, 64 B per row; logical chunk c of row r sits in slot
-//            c ^ ((r >> 2) & 3). A fragments are read with ds_read_b128
-//            (8 consecutive k of one row per lane).
+//            c ^ ((r >> 2) & 1) ^ 3 ((r >> 3) & 1). A fragments are read with
+//            ds_read_b128 (8 consecutive k of one row per lane).
 //   B stage: 32 k rows x BN n; logical chunk c of row k sits in slot
-//            c ^ (10 (k & 1) + 4 ((k >> 1) & 1)). B fragments need 8 consecutive
-//            k of one column per lane; ds_read_b64_tr_b16 delivers them from the
-//            row-major (n-contiguous) tile: in each 16-lane group, lane L reads 4
-//            n values of row L/4 and lane i receives column i of the 4 x 16 block.
-// The MFMA is issued with the B fragment as its first operand, so the
-// accumulator of lane l holds four consecutive n of row m = l % 32, which the
+//            c ^ s(k), s(k) = (10 (k & 1) + 4 ((k >> 1) & 1)) ^ 2 ((k >> 3) & 1).
+//            B fragments need 8 consecutive k of one column per lane;
+//            ds_read_b64_tr_b16 delivers them from the row-major (n-contiguous)
+//            tile: in each 16-lane group, lane L reads 4 n values of row L/4 and
+//            lane i receives column i of the 4 x 16 block.
+// The MFMA is issued with the B fragment as its first operand, so each group of
+// four accumulators of a lane holds four consecutive n of one row m, which the
 // epilogue writes as one 16-byte store.
 //
 // Work units. The schedulers hand out work units; a unit is one work item, or
@@ -41,19 +43,24 @@
 
 namespace ptg {
 
-// Tile shape and wave grid. A workgroup has WAVES_M x WAVES_N wave64s; each
-// wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of the output tile.
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+// Tile shape, wave grid and MFMA shape. A workgroup has WAVES_M x WAVES_N
+// wave64s; each wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of the output
+// tile, made of MB x MB MFMA blocks: MB = 32 uses v_mfma_f32_32x32x16_bf16 (two
+// MFMAs per 32-deep stage), MB = 16 uses v_mfma_f32_16x16x32_bf16 (one).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MB_>
 struct Cfg {
   static constexpr int BM_ = BM, BN_ = BN, WAVES_N_ = WAVES_N;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * NW;
   static constexpr int BK = 32, NSTAGE = 4;          // k per stage, LDS stages
+  static constexpr int MB = MB_, KS = 512 / MB_;     // MFMA block edge, k per MFMA
+  static constexpr int ACC_N = MB * MB / 64;         // accumulator floats per lane per block
+  static constexpr int QUADS = ACC_N / 4;            // 16-byte groups of them
   static constexpr int A_ROW = BK * 2;              // bytes per row of the A stage
   static constexpr int A_ROW_CHUNKS = BK / 8;
   static constexpr int A_RPL = 1024 / A_ROW;         // A rows one wave-load (64 x 16 B) covers
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
-  static constexpr int MI = WM / 32, NI = WN / 32;            // 32x32 MFMA blocks per wave
+  static constexpr int MI = WM / MB, NI = WN / MB;            // MFMA blocks per wave
   static constexpr int A_LOADS = BM * (BK / 8) / THREADS;     // 16-byte loads per thread per stage
   static constexpr int B_LOADS = BK * (BN / 8) / THREADS;
   static constexpr int A_STAGE = BM * BK * 2;       // bytes
@@ -63,25 +70,27 @@ struct Cfg {
   static constexpr int STAGE = A_STAGE + B_STAGE;
   static constexpr int LDS = NSTAGE * STAGE;
   static_assert(A_LOADS * THREADS == BM * (BK / 8) && B_LOADS * THREADS == BK * (BN / 8), "load split");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(WM % MB == 0 && WN % MB == 0 && (MB == 16 || MB == 32), "wave tile");
 };
 
-// The wave grid used for each tile edge: 128 -> 2 x 2 waves (64 x 64 each);
-// 256 -> 2 x 4 waves (128 x 64 each), i.e. two waves per SIMD, so one wave's
-// MFMAs can issue while the other waits to issue its memory instructions.
+// The wave grid used for each tile edge: 128 -> 2 x 2 waves of 64 x 64 in
+// 32 x 32 blocks (two workgroups per CU, so two waves share each SIMD); 256 ->
+// 2 x 2 waves of 128 x 128 in 16 x 16 blocks (one wave per SIMD, 256
+// accumulator registers each). The large wave tile reads two thirds of the LDS
+// bytes per flop that 128 x 64 wave tiles need, and the part is power-bound,
+// so fewer LDS bytes buy clock.
 template <int EDGE> struct TileCfg;
-template <> struct TileCfg<128> { using type = Cfg<128, 128, 2, 2>; };
-#ifndef PTG_WAVES_256
-#define PTG_WAVES_256 8
-#endif
-#if PTG_WAVES_256 == 8
-template <> struct TileCfg<256> { using type = Cfg<256, 256, 2, 4>; };
-#else
-template <> struct TileCfg<256> { using type = Cfg<256, 256, 2, 2>; };
-#endif
+template <> struct TileCfg<128> { using type = Cfg<128, 128, 2, 2, 32>; };
+template <> struct TileCfg<256> { using type = Cfg<256, 256, 2, 2, 16>; };
 
-__device__ __forceinline__ uint32_t swz_a(uint32_t row) { return (row >> 2) & 3u; }
-__device__ __forceinline__ uint32_t swz_b(uint32_t k) { return 10u * (k & 1u) + 4u * ((k >> 1) & 1u); }
+// A: rows r and r + 8 share banks, and a 16 x 16 fragment read takes chunks
+// {0, 2} (or {1, 3}) of the same 16 rows in one pass, so flipping row bit 3
+// flips both slot bits; row bit 2 flips slot bit 0 (4 rows of 64 B fill the
+// banks once).
+__device__ __forceinline__ uint32_t swz_a(uint32_t row) { return ((row >> 2) & 1u) ^ (3u * ((row >> 3) & 1u)); }
+__device__ __forceinline__ uint32_t swz_b(uint32_t k) {
+  return (10u * (k & 1u) + 4u * ((k >> 1) & 1u)) ^ (2u * ((k >> 3) & 1u));
+}
 
 // One record of the claim ring: the answer to one claim. `valid` is the success
 // predicate; `tile` is meaningful only when valid. `seq` is the worker's tile
@@ -311,19 +320,23 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     };
 
     // ---- per-thread load addressing for this tile. Load j of a wave moves a
-    // 1 KiB block: A rows (j*4+wave)*8 .. +8 (8 lanes per 128-byte row), B k rows
-    // (j*4+wave)*(64/B_ROW_CHUNKS*...) (B_ROW_CHUNKS lanes per row). The swizzle
-    // of A depends on j only through j's parity and that of B not at all, so the
-    // per-load voffset is one of two (A) or one (B) per-lane bases plus a
-    // wave-uniform step.
+    // 1 KiB block: A rows (j*NW+wave)*A_RPL .. +A_RPL (A_ROW_CHUNKS lanes per row),
+    // B k rows (j*NW+wave)*kBRowsPerLoad .. (B_ROW_CHUNKS lanes per row). Each
+    // lane fetches the global chunk whose swizzled slot is its own LDS position.
+    // The A swizzle does not change between loads (they step by a multiple of 16
+    // rows); the B swizzle flips its bit 1 when a load's k rows step by an odd
+    // multiple of 8, so B has two per-lane bases. Each voffset is one of them
+    // plus a wave-uniform step.
     constexpr uint32_t kBRowsPerLoad = 64u / CF::B_ROW_CHUNKS;  // k rows one wave-load covers
+    constexpr uint32_t kBRowsPerJ = (uint32_t)CF::NW * kBRowsPerLoad;
     const uint32_t a_row0 = wave * (uint32_t)CF::A_RPL + lane / CF::A_ROW_CHUNKS;  // row of load j = a_row0 + RPL NW j
     const uint32_t a_c0 = (lane % CF::A_ROW_CHUNKS) ^ swz_a(a_row0);
     const uint32_t a_base = a_row0 * (uint32_t)K * 2u;
-    const uint32_t b_k0 = wave * kBRowsPerLoad + lane / CF::B_ROW_CHUNKS;  // k row of load j = b_k0 + NW*kBRowsPerLoad j
-    const uint32_t b_c = (lane % CF::B_ROW_CHUNKS) ^ swz_b(b_k0);
-    const bool b_col_ok = n0 + (int32_t)(b_c * 8u) < N;
-    const uint32_t b_base = b_col_ok ? (b_k0 * (uint32_t)N + b_c * 8u) * 2u : kBufOob;
+    const uint32_t b_k0 = wave * kBRowsPerLoad + lane / CF::B_ROW_CHUNKS;  // k row of load j = b_k0 + kBRowsPerJ j
+    const uint32_t b_c0 = (lane % CF::B_ROW_CHUNKS) ^ swz_b(b_k0);
+    const uint32_t b_c1 = b_c0 ^ 2u;  // the chunk when k row bit 3 is flipped
+    const uint32_t b_base0 = n0 + (int32_t)(b_c0 * 8u) < N ? (b_k0 * (uint32_t)N + b_c0 * 8u) * 2u : kBufOob;
+    const uint32_t b_base1 = n0 + (int32_t)(b_c1 * 8u) < N ? (b_k0 * (uint32_t)N + b_c1 * 8u) * 2u : kBufOob;
     const int32_t m_left = M - m0;  // rows of A that exist in this tile
     const uint16_t *a_tile = pb.A + (size_t)m0 * (size_t)K;
     const uint16_t *b_tile = pb.B + n0;
@@ -334,7 +347,9 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     const int32_t ke = split ? (int32_t)((uint32_t)nk * (chunk + 1u) / (uint32_t)args.split_chunks) : nk;
 
     // voffset of load j (A loads first, then B) for k-step kt; chunks outside
-    // the matrix (row / column edges, K tail) read as zero via kBufOob.
+    // the matrix (row / column edges, K tail) read as zero via kBufOob. Every
+    // chunk of a k-step past the unit's end reads as zero through its resource
+    // (record count 0).
     auto load_voff = [&](int j, int32_t kt) -> uint32_t {
       const int32_t k0 = kt * CF::BK;
       const bool tail = kt >= full;
@@ -347,9 +362,10 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         return out ? kBufOob : vo;
       }
       const int jb = j - CF::A_LOADS;
-      const uint32_t krow = b_k0 + (uint32_t)CF::NW * kBRowsPerLoad * (uint32_t)jb;
-      const uint32_t vo = b_base + (uint32_t)jb * (uint32_t)CF::NW * kBRowsPerLoad * (uint32_t)N * 2u;
-      const bool out = b_base == kBufOob || (tail && k0 + (int32_t)krow >= K);
+      const uint32_t krow = b_k0 + kBRowsPerJ * (uint32_t)jb;
+      const uint32_t bb = ((kBRowsPerJ * (uint32_t)jb) & 8u) ? b_base1 : b_base0;
+      const uint32_t vo = bb + (uint32_t)jb * kBRowsPerJ * (uint32_t)N * 2u;
+      const bool out = bb == kBufOob || (tail && k0 + (int32_t)krow >= K);
       return out ? kBufOob : vo;
     };
     auto load_dst = [&](int j) -> uint32_t {
@@ -359,98 +375,101 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // all loads of k-step kt into stage dst, back to back (prologue)
     auto issue_all = [&](int st, int32_t kt) {
       unsigned char *dst = smem + st * CF::STAGE;
-      const i32x4 ra = make_rsrc_words(a_tile + kt * CF::BK);
-      const i32x4 rb = make_rsrc_words(b_tile + (size_t)(kt * CF::BK) * (size_t)N);
+      const i32x4 ra = make_rsrc_words(a_tile + kt * CF::BK, kt < ke);
+      const i32x4 rb = make_rsrc_words(b_tile + (size_t)(kt * CF::BK) * (size_t)N, kt < ke);
       const uint32_t base = lds_addr(dst);
 #pragma unroll
       for (int j = 0; j < CF::A_LOADS + CF::B_LOADS; ++j)
         load16_to_lds(j < CF::A_LOADS ? ra : rb, base + load_dst(j), load_voff(j, kt));
     };
 
-    // fragment read offsets (bytes inside a stage)
+    // fragment read offsets (bytes inside a stage). An MFMA operand is 8
+    // consecutive k per lane: lanes l and l + MB hold the next 8 k of the same
+    // row (A) or column (B).
     uint32_t off_a[CF::MI];
     uint32_t swa[CF::MI];
 #pragma unroll
     for (int mi = 0; mi < CF::MI; ++mi) {
-      const uint32_t row = wm * CF::WM + mi * 32 + (lane & 31u);
+      const uint32_t row = wm * CF::WM + mi * CF::MB + (lane % CF::MB);
       off_a[mi] = row * (uint32_t)CF::A_ROW;
-      swa[mi] = swz_a(row) ^ (lane >> 5);
+      swa[mi] = swz_a(row) ^ (lane / CF::MB);
     }
     uint32_t off_b[CF::NI];
     {
-      const uint32_t q = lane >> 4, i = lane & 15u, h = q >> 1;
-      const uint32_t kk = 8u * h + (i >> 2);
+      // 32 x 32 blocks: lane group q = lane / 16 covers k half q / 2 and column
+      // half q % 2; 16 x 16 blocks: k quarter q of all 16 columns
+      const uint32_t q = lane >> 4, i = lane & 15u;
+      const uint32_t kk = CF::MB == 32 ? 8u * (q >> 1) + (i >> 2) : 8u * q + (i >> 2);
 #pragma unroll
       for (int ni = 0; ni < CF::NI; ++ni) {
-        const uint32_t n = wn * CF::WN + ni * 32 + 16u * (q & 1u) + 4u * (i & 3u);
+        const uint32_t n = CF::MB == 32 ? wn * CF::WN + ni * 32 + 16u * (q & 1u) + 4u * (i & 3u)
+                                        : wn * CF::WN + ni * 16 + 4u * (i & 3u);
         off_b[ni] = kk * CF::B_ROW + (((n >> 3) ^ swz_b(kk)) << 4) + ((n & 7u) << 1);
       }
     }
 
     // A fragment: 8 consecutive k of one row (ds_read_b128). B fragment: two
-    // transposing reads of 4 k each (ds_read_b64_tr_b16) for one column.
-    // Optionally, loads [first, first+count) of k-step kt_load into stage ldst
-    // are placed in program order between the reads; the reads alternate with
-    // MFMAs, so the loads land between MFMAs instead of in one burst.
+    // transposing reads of 4 k each (ds_read_b64_tr_b16) for one column. s
+    // selects the MFMA's k slice of the stage. Optionally, the loads of k-step
+    // kt_load into stage lst are placed in program order between the reads
+    // (32 x 32 blocks: load j after read j; 16 x 16: after read j * kReads /
+    // count, spread over the step's reads); the reads alternate
+    // with MFMAs, so the loads land between MFMAs instead of in one burst.
+    constexpr int kReads = CF::MI + 2 * CF::NI;
     auto read_frags = [&](int st, int s, bf16x8(&af)[CF::MI], bf16x8(&bfr)[CF::NI], int lst, int32_t kt_load,
-                          int first, int count) {
+                          int count) {
       const unsigned char *sa = smem + st * CF::STAGE;
       const unsigned char *sb = sa + CF::A_STAGE;
       i32x4 ra = {0, 0, 0, 0}, rb = {0, 0, 0, 0};
       uint32_t lbase = 0;
       if (count > 0) {
-        ra = make_rsrc_words(a_tile + kt_load * CF::BK);
-        rb = make_rsrc_words(b_tile + (size_t)(kt_load * CF::BK) * (size_t)N);
+        ra = make_rsrc_words(a_tile + kt_load * CF::BK, kt_load < ke);
+        rb = make_rsrc_words(b_tile + (size_t)(kt_load * CF::BK) * (size_t)N, kt_load < ke);
         lbase = lds_addr(smem + lst * CF::STAGE);
       }
+      i16x4 lo[CF::NI];
 #pragma unroll
-      for (int mi = 0; mi < CF::MI; ++mi) {
-        af[mi] = *(const bf16x8 *)(sa + off_a[mi] + ((((uint32_t)(2 * s)) ^ swa[mi]) << 4));
-        if (mi < count) {
-          const int j = first + mi;
-          load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
+      for (int r = 0; r < kReads; ++r) {
+        if (r < CF::MI) {
+          af[r] = *(const bf16x8 *)(sa + off_a[r] + ((((uint32_t)((CF::KS / 8) * s)) ^ swa[r]) << 4));
+        } else {
+          const int ni = (r - CF::MI) >> 1;
+          const unsigned char *pb0 = sb + off_b[ni] + (CF::KS * s) * CF::B_ROW;
+          if (((r - CF::MI) & 1) == 0) {
+            lo[ni] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0));
+          } else {
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0 + 4 * CF::B_ROW));
+            typedef __attribute__((ext_vector_type(8))) short i16x8;
+            const i16x8 v = __builtin_shufflevector(lo[ni], hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            bfr[ni] = __builtin_bit_cast(bf16x8, v);
+          }
         }
-      }
 #pragma unroll
-      for (int ni = 0; ni < CF::NI; ++ni) {
-        const unsigned char *pb0 = sb + off_b[ni] + (16 * s) * CF::B_ROW;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0));
-        if (CF::MI + 2 * ni < count) {
-          const int j = first + CF::MI + 2 * ni;
-          load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
-        }
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0 + 4 * CF::B_ROW));
-        if (CF::MI + 2 * ni + 1 < count) {
-          const int j = first + CF::MI + 2 * ni + 1;
-          load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
-        }
-        typedef __attribute__((ext_vector_type(8))) short i16x8;
-        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        bfr[ni] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int r = CF::MI + 2 * CF::NI; r < CF::A_LOADS + CF::B_LOADS; ++r) {
-        if (r < count) {
-          const int j = first + r;
-          load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
-        }
+        for (int j = 0; j < count; ++j)
+          if ((CF::MB == 32 ? j : j * kReads / count) == r)
+            load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
       }
     };
 
-    f32x16 acc[CF::MI][CF::NI];
+    typedef float accv __attribute__((ext_vector_type(CF::ACC_N)));
+    accv acc[CF::MI][CF::NI];
 #pragma unroll
     for (int mi = 0; mi < CF::MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < CF::NI; ++ni)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
+        for (int e = 0; e < CF::ACC_N; ++e) acc[mi][ni][e] = 0.0f;
 
     auto mma = [&](const bf16x8(&af)[CF::MI], const bf16x8(&bfr)[CF::NI]) {
 #pragma unroll
       for (int mi = 0; mi < CF::MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < CF::NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+        for (int ni = 0; ni < CF::NI; ++ni) {
+          if constexpr (CF::MB == 32)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+          else
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+        }
     };
 
     // the prefetch claim is issued claim_lead k-steps before the tile ends (the
@@ -460,44 +479,128 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     const int32_t claim_at = !last_sub ? -1 : ke - kb > args.claim_lead ? ke - args.claim_lead : kb;
     if (ke == kb && last_sub) do_claims();
 
-    if (ke > kb) {
-      // four 32-deep stages: the loads of k-step kt+3 go out during k-step kt
-      // into the stage k-step kt-1 just left, so a load has three k-steps to land
-      constexpr int kLoads = CF::A_LOADS + CF::B_LOADS;
-      constexpr int kReads = CF::MI + 2 * CF::NI;
-      constexpr int kMfma = CF::MI * CF::NI;
-      static_assert(CF::NSTAGE == 4 && kLoads == 4, "stage ring");
-      issue_all(0, kb);
-      issue_all(1, kb + 1 < ke ? kb + 1 : ke - 1);
-      issue_all(2, kb + 2 < ke ? kb + 2 : ke - 1);
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      wg_barrier();
-      bf16x8 a0[CF::MI], b0[CF::NI], a1[CF::MI], b1[CF::NI];
-      read_frags(0, 0, a0, b0, 0, 0, 0, 0);
-      for (int32_t kt = kb; kt < ke; ++kt) {
-        const int st = (kt - kb) & 3;
-        if (kt == claim_at) do_claims();
-        const int32_t kl = kt + 3 < ke ? kt + 3 : ke - 1;
-        read_frags(st, 1, a1, b1, (st + 3) & 3, kl, 0, kLoads);
-        mma(a0, b0);
-        interleave<kReads, kMfma>();
-        // stage st fully read and stage st+1 landed (its loads went out two k-steps
-        // ago; the eight loads issued since may still be in flight)
-        wait_lds_all();
+    constexpr int kLoads = CF::A_LOADS + CF::B_LOADS;
+    constexpr int kMfma = CF::MI * CF::NI;
+    static_assert(CF::NSTAGE == 4, "stage ring");
+    if constexpr (CF::MB == 32) {
+      if (ke > kb) {
+        // four 32-deep stages: the loads of k-step kt+3 go out during k-step kt
+        // into the stage k-step kt-1 just left, so a load has three k-steps to land;
+        // each k-step is two 16-deep MFMA slices, and the fragments of one slice
+        // are read while the other's MFMAs run
+        static_assert(kLoads == 4, "stage ring");
+        issue_all(0, kb);
+        issue_all(1, kb + 1);
+        issue_all(2, kb + 2);
         asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         wg_barrier();
-        read_frags((st + 1) & 3, 0, a0, b0, 0, 0, 0, 0);
-        mma(a1, b1);
-        interleave<kReads, kMfma>();
+        bf16x8 a0[CF::MI], b0[CF::NI], a1[CF::MI], b1[CF::NI];
+        read_frags(0, 0, a0, b0, 0, 0, 0);
+        for (int32_t kt = kb; kt < ke; ++kt) {
+          const int st = (kt - kb) & 3;
+          if (kt == claim_at) do_claims();
+          read_frags(st, 1, a1, b1, (st + 3) & 3, kt + 3, kLoads);
+          mma(a0, b0);
+          interleave<kReads, kMfma>();
+          // stage st fully read and stage st+1 landed (its loads went out two k-steps
+          // ago; the eight loads issued since may still be in flight)
+          wait_lds_all();
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+          wg_barrier();
+          read_frags((st + 1) & 3, 0, a0, b0, 0, 0, 0);
+          mma(a1, b1);
+          interleave<kReads, kMfma>();
+        }
+      }
+    } else {
+      if (ke > kb) {
+        // four 32-deep stages, one 32-deep MFMA per block and k-step: the
+        // fragments of k-step kt+1 are read from its stage while step kt's MFMAs
+        // run on the fragments read during step kt-1. The loads of step kt+4 go
+        // out during step kt into the stage step kt's fragments came from (every
+        // wave finished reading it before the barrier that ended step kt-1), and
+        // must have landed by the barrier that ends step kt+2: between two and
+        // three k-steps in flight.
+        static_assert(kLoads == 8, "stage ring");
+        issue_all(0, kb);
+        issue_all(1, kb + 1);
+        issue_all(2, kb + 2);
+        issue_all(3, kb + 3);
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // stages 0 and 1 landed
+        wg_barrier();
+        bf16x8 a0[CF::MI], b0[CF::NI], a1[CF::MI], b1[CF::NI];
+        read_frags(0, 0, a0, b0, 0, 0, 0);
+        wait_lds_all();
+        wg_barrier();  // stage 0 read by every wave before step kb's loads refill it
+        auto step = [&](int32_t kt, const bf16x8(&ac)[CF::MI], const bf16x8(&bc)[CF::NI], bf16x8(&an)[CF::MI],
+                        bf16x8(&bn)[CF::NI]) {
+          const int st = (kt - kb) & 3;
+          if (kt == claim_at) do_claims();
+          read_frags((st + 1) & 3, 0, an, bn, st, kt + 4, kLoads);
+          mma(ac, bc);
+          interleave<kReads, kMfma>();
+          // stage st+1 fully read and stage st+2 landed (the sixteen loads of the
+          // two steps since its own may still be in flight); the step's MFMAs
+          // are all issued first (no instruction moves across the fence)
+          __builtin_amdgcn_sched_barrier(0);
+          wait_lds_all();
+          asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+          wg_barrier();
+        };
+        // two steps per trip, so the fragment buffers swap roles by name. An odd
+        // count ends with one step past the unit: its stage was zero-filled, and
+        // adding zero products leaves every accumulator bit for bit as it was.
+        for (int32_t kt = kb; kt < ke; kt += 2) {
+          step(kt, a0, b0, a1, b1);
+          step(kt + 1, a1, b1, a0, b0);
+        }
       }
     }
 
-    // ---- K-chunk of a split tile: publish the partial sum; the workgroup that
-    // completes the tile's last chunk adds all partials in chunk order and writes
-    // C. The order is fixed, so the result does not depend on who finished last.
-    // Partial slots are thread-major per 16-byte group: fully coalesced.
-    bool write_c = true;
-    if (split) {
+    // ---- publish the claims issued during this unit (producer, wave 0): each
+    // answer goes to its ring record. Prefetch claims are resolved here, before
+    // the epilogue: reading an atomic's answer waits for every older memory
+    // operation of the wave, and the C stores would otherwise be among them.
+    auto publish_claims = [&]() {
+      for (uint32_t b = 0; b < batch_n; ++b) {
+        const uint32_t v = claim_resolve(args, xcc, lane, b == 0 ? batch[0] : batch[1], region);
+        const uint32_t ok = v < (uint32_t)T ? 1u : 0u;
+        if (!ok) failed = true;
+        if (lane == 0) ring[(batch_ord + b) % (uint32_t)args.ring_depth] = RingRec{v, ok, batch_ord + b, 0u};
+      }
+    };
+    if constexpr (MODE == kDynamic) {
+      if (wave == 0 && args.claims_ahead >= 1) publish_claims();
+    }
+
+    // ---- epilogue: fp32 accumulators -> C. Lane l holds, in each group of four
+    // accumulators, 4 consecutive n of row m = l % MB: n = 8 qd + 4 (l / 32) for
+    // 32 x 32 blocks, 4 (l / 16) for 16 x 16 blocks. Group g = (mi NI + ni)
+    // QUADS + qd of a thread is its g-th 16-byte store.
+    const bool interior = m0 + BM <= M && n0 + BN <= N;
+    auto store_group = [&](int mi, int ni, int qd, const f32x4 &v) {
+      const int32_t m = m0 + (int32_t)(wm * CF::WM + mi * CF::MB + (lane % CF::MB));
+      const int32_t n = n0 + (int32_t)(wn * CF::WN + ni * CF::MB + 8 * qd + 4 * (lane / CF::MB));
+      if (interior || (m < M && n < N)) *(f32x4 *)(pb.C + (size_t)m * (size_t)N + n) = v;
+    };
+
+    if (!split) {
+#pragma unroll
+      for (int mi = 0; mi < CF::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < CF::NI; ++ni)
+#pragma unroll
+          for (int qd = 0; qd < CF::QUADS; ++qd)
+            store_group(mi, ni, qd, f32x4{acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1], acc[mi][ni][4 * qd + 2],
+                                          acc[mi][ni][4 * qd + 3]});
+    } else {
+      // K-chunk of a split tile: publish the partial sum; the workgroup that
+      // completes the tile's last chunk adds all partials in chunk order and
+      // writes C. The order is fixed, so the result does not depend on who
+      // finished last. Partial slots are thread-major per 16-byte group: fully
+      // coalesced. The sum reads the slots (this workgroup's own partial
+      // included) in batches of up to 16 groups per thread, all of a chunk's
+      // loads of a batch in flight at once; the accumulators are not touched.
       const uint32_t S = (uint32_t)args.split_chunks;
       const uint32_t q = tile - (uint32_t)args.split_base;
       f32x4 *slot = reinterpret_cast<f32x4 *>(args.ws) + (size_t)(item - (uint32_t)args.split_base) * (BM * BN / 4);
@@ -506,8 +609,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 #pragma unroll
         for (int ni = 0; ni < CF::NI; ++ni)
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int g = (mi * CF::NI + ni) * 4 + qd;
+          for (int qd = 0; qd < CF::QUADS; ++qd) {
+            const int g = (mi * CF::NI + ni) * CF::QUADS + qd;
             slot[g * CF::THREADS + tid] = f32x4{acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1],
                                                 acc[mi][ni][4 * qd + 2], acc[mi][ni][4 * qd + 3]};
           }
@@ -518,52 +621,36 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         split_last = prev + 1u == S ? 1u : 0u;
       }
       __syncthreads();
-      write_c = wave_uniform(split_last) != 0;
-      if (write_c) {
+      if (wave_uniform(split_last) != 0) {
         __threadfence();  // acquire the other chunks' partials
-        const f32x4 *base = reinterpret_cast<const f32x4 *>(args.ws) + (size_t)q * S * (BM * BN / 4);
+        const f32x4 *base = reinterpret_cast<const f32x4 *>(args.ws) + (size_t)q * S * (BM * BN / 4) + tid;
+        constexpr int kGroups = CF::MI * CF::NI * CF::QUADS;
+        constexpr int kBatch = kGroups < 16 ? kGroups : 16;
+        static_assert(kGroups % kBatch == 0, "batches");
+        for (int g0 = 0; g0 < kGroups; g0 += kBatch) {
+          f32x4 v[kBatch];
 #pragma unroll
-        for (int mi = 0; mi < CF::MI; ++mi)
+          for (int i = 0; i < kBatch; ++i) v[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          for (uint32_t c = 0; c < S; ++c) {
+            const f32x4 *src = base + (size_t)c * (BM * BN / 4) + (size_t)g0 * CF::THREADS;
+            f32x4 p[kBatch];
 #pragma unroll
-          for (int ni = 0; ni < CF::NI; ++ni)
+            for (int i = 0; i < kBatch; ++i) p[i] = src[(size_t)i * CF::THREADS];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
-        for (uint32_t c = 0; c < S; ++c) {
-          const f32x4 *src = base + (size_t)c * (BM * BN / 4);
+            for (int i = 0; i < kBatch; ++i)
 #pragma unroll
-          for (int mi = 0; mi < CF::MI; ++mi) {
+              for (int e = 0; e < 4; ++e) v[i][e] += p[i][e];
+          }
 #pragma unroll
-            for (int ni = 0; ni < CF::NI; ++ni)
-#pragma unroll
-              for (int qd = 0; qd < 4; ++qd) {
-                const f32x4 v = src[((mi * CF::NI + ni) * 4 + qd) * CF::THREADS + tid];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[mi][ni][4 * qd + e] += v[e];
-              }
+          for (int i = 0; i < kBatch; ++i) {
+            const int g = g0 + i;
+            store_group(g / (CF::NI * CF::QUADS), (g / CF::QUADS) % CF::NI, g % CF::QUADS, v[i]);
           }
         }
       }
     }
 
-    // ---- epilogue: fp32 accumulators -> C (lane holds 4 consecutive n of one m)
-    const bool interior = m0 + BM <= M && n0 + BN <= N;
-#pragma unroll
-    for (int mi = 0; mi < CF::MI && write_c; ++mi) {
-      const int32_t m = m0 + (int32_t)(wm * CF::WM + mi * 32 + (lane & 31u));
-      float *crow = pb.C + (size_t)m * (size_t)N;
-#pragma unroll
-      for (int ni = 0; ni < CF::NI; ++ni) {
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int32_t n = n0 + (int32_t)(wn * CF::WN + ni * 32 + 8 * qd + 4 * (lane >> 5));
-          const f32x4 v = {acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1], acc[mi][ni][4 * qd + 2],
-                           acc[mi][ni][4 * qd + 3]};
-          if (interior || (m < M && n < N)) *(f32x4 *)(crow + n) = v;
-        }
-      }
-    }
-
-    // ---- publish the next claim (producer) and log the tile
+    // ---- claims after the work (claims_ahead = 0): issue and publish
     if (wave == 0) {
       if constexpr (MODE == kDynamic) {
         if (args.claims_ahead == 0 && !failed && last_sub) {
@@ -571,15 +658,11 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
           batch[0] = claim_issue(args, region, lane);
           batch_n = 1;
           ++next_ord;
-        }
-        for (uint32_t b = 0; b < batch_n; ++b) {
-          const uint32_t v = claim_resolve(args, xcc, lane, b == 0 ? batch[0] : batch[1], region);
-          const uint32_t ok = v < (uint32_t)T ? 1u : 0u;
-          if (!ok) failed = true;
-          if (lane == 0) ring[(batch_ord + b) % (uint32_t)args.ring_depth] = RingRec{v, ok, batch_ord + b, 0u};
+          publish_claims();
         }
       }
     }
+    // ---- log the tile
     if (tid == 0) {
       const uint64_t t1 = clock_core();
       const uint64_t r1 = clock_wall();

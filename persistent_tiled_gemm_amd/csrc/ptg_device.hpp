@@ -42,6 +42,14 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void *base) {
   return r;
 }
 
+// The same with a record count of zero when !live: every load through it then
+// reads zeros (a whole k-step masked with one scalar select, no branch).
+__device__ __forceinline__ i32x4 make_rsrc_words(const void *base, bool live) {
+  i32x4 r = make_rsrc_words(base);
+  r[2] = live ? (int)kBufRecords : 0;
+  return r;
+}
+
 template <typename T>
 __device__ __forceinline__ T *uniform_ptr(T *p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);

@@ -110,7 +110,11 @@ def test_tail_split_shortens_the_partial_wave():
     model_split = simulate([(e - b) / nk for _, b, e in units], "dynamic", slots=256).makespan
     say(f"  whole {res['whole'][0] / t:.2f} t (model {model_whole}), split {res['split'][0] / t:.2f} t "
         f"(model without the fix-up {model_split})")
-    assert 0.8 * model_whole <= res["whole"][0] / t <= 1.15 * model_whole
+    # whole tiles: the 257th tile starts only when a first-wave tile ends. It then
+    # runs alone; this shape is bound by memory bandwidth, which a lone tile does
+    # not share, so it takes well under t and the run lands between 1.3 t and
+    # the equal-cost model's 2 t
+    assert 1.3 <= res["whole"][0] / t <= 1.15 * model_whole
     # the fix-up (one workgroup adding the chunks' partial tiles) is not in the model: it costs
     # about one partial tile's round trip through memory per chunk
     assert res["split"][0] < 0.95 * res["whole"][0]
