@@ -12,8 +12,9 @@
 // LDS layouts (16-byte chunks, XOR-swizzled so fragment reads are bank-conflict
 // free):
 //   A stage: BM rows x 32 k, 64 B per row; logical chunk c of row r sits in slot
-//            c ^ ((r >> 2) & 1) ^ 3 ((r >> 3) & 1). A fragments are read with
-//            ds_read_b128 (8 consecutive k of one row per lane).
+//            c ^ ((r >> 1) & 3) (16 x 16 blocks) or c ^ ((r >> 2) & 3) (32 x 32).
+//            A fragments are read with ds_read_b128 (8 consecutive k of one row
+//            per lane).
 //   B stage: 32 k rows x BN n; logical chunk c of row k sits in slot
 //            c ^ s(k), s(k) = (10 (k & 1) + 4 ((k >> 1) & 1)) ^ 2 ((k >> 3) & 1).
 //            B fragments need 8 consecutive k of one column per lane;
@@ -83,11 +84,13 @@ template <int EDGE> struct TileCfg;
 template <> struct TileCfg<128> { using type = Cfg<128, 128, 2, 2, 32>; };
 template <> struct TileCfg<256> { using type = Cfg<256, 256, 2, 2, 16>; };
 
-// A: rows r and r + 8 share banks, and a 16 x 16 fragment read takes chunks
-// {0, 2} (or {1, 3}) of the same 16 rows in one pass, so flipping row bit 3
-// flips both slot bits; row bit 2 flips slot bit 0 (4 rows of 64 B fill the
-// banks once).
-__device__ __forceinline__ uint32_t swz_a(uint32_t row) { return ((row >> 2) & 1u) ^ (3u * ((row >> 3) & 1u)); }
+// A: the slot XOR for row r depends on the fragment read pattern. Measured with
+// the LDS bank-conflict counter on gfx950 (ds_read_b128, 64 B rows): for 32 x 32
+// blocks (32 rows x one chunk per half-wave) (r >> 2) & 3 is conflict-free and
+// (r >> 1) & 3 is two-way; for 16 x 16 blocks (16 rows x four chunks) it is the
+// other way round, and no XOR at all is two-way.
+template <int MB>
+__device__ __forceinline__ uint32_t swz_a(uint32_t row) { return MB == 32 ? (row >> 2) & 3u : (row >> 1) & 3u; }
 __device__ __forceinline__ uint32_t swz_b(uint32_t k) {
   return (10u * (k & 1u) + 4u * ((k >> 1) & 1u)) ^ (2u * ((k >> 3) & 1u));
 }
@@ -175,6 +178,27 @@ __device__ __forceinline__ uint32_t claim_resolve(const KernelArgs &a, uint32_t 
   }
   return T;
 }
+// claim_issue's atomic as one assembly statement that skips itself unless
+// `now` (wave-uniform) is set: lane 0 alone adds 1 to *ctr (exec is narrowed
+// inside the statement) and receives the old value in `ret`. A main-loop step
+// that claims thus stays one basic block; a branch around the claim would split
+// it, and the register allocator then copies accumulators around the split. The
+// compiler does not see the atomic: the caller waits (vmcnt) before reading ret.
+__device__ __forceinline__ void claim_issue_asm(uint32_t *ctr, bool now, uint32_t &ret) {
+  uint64_t saved;
+  asm volatile(
+      "s_cmp_eq_u32 %[now], 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "s_mov_b64 %[saved], exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %[ret], %[off], %[one], %[ctr] sc0\n\t"
+      "s_mov_b64 exec, %[saved]\n"
+      "1:"
+      : [ret] "+v"(ret), [saved] "=&s"(saved)
+      : [now] "s"(__builtin_amdgcn_readfirstlane(now ? 1u : 0u)), [off] "v"(0u), [one] "v"(1u), [ctr] "s"(ctr)
+      : "memory", "scc");
+}
+
 __device__ __forceinline__ uint32_t claim_next(const KernelArgs &a, uint32_t xcc, uint32_t lane, uint32_t &region) {
   return claim_resolve(a, xcc, lane, claim_issue(a, region, lane), region);
 }
@@ -305,16 +329,25 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // ---- claim ahead (the throttle: at most claims_ahead beyond the current tile)
     uint32_t batch[2] = {0u, 0u};  // raw answers of the claims issued during this tile (lane 0)
     uint32_t batch_ord = 0, batch_n = 0;
-    auto do_claims = [&]() {
+    // reserve: the ordinals of the claims this unit sends (wave 0, scalar)
+    auto reserve_claims = [&]() {
       if constexpr (MODE == kDynamic) {
         if (wave == 0 && !failed && args.claims_ahead >= 1) {
           batch_ord = next_ord;
           while (next_ord <= ord + (uint32_t)args.claims_ahead && batch_n < 2) {
-            const uint32_t v = claim_issue(args, region, lane);
-            if (batch_n == 0) batch[0] = v; else batch[1] = v;
             ++batch_n;
             ++next_ord;
           }
+        }
+      }
+    };
+    // reserve and send at once
+    auto do_claims = [&]() {
+      if constexpr (MODE == kDynamic) {
+        reserve_claims();
+        for (uint32_t b = 0; b < batch_n; ++b) {
+          const uint32_t v = claim_issue(args, region, lane);
+          if (b == 0) batch[0] = v; else batch[1] = v;
         }
       }
     };
@@ -330,7 +363,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     constexpr uint32_t kBRowsPerLoad = 64u / CF::B_ROW_CHUNKS;  // k rows one wave-load covers
     constexpr uint32_t kBRowsPerJ = (uint32_t)CF::NW * kBRowsPerLoad;
     const uint32_t a_row0 = wave * (uint32_t)CF::A_RPL + lane / CF::A_ROW_CHUNKS;  // row of load j = a_row0 + RPL NW j
-    const uint32_t a_c0 = (lane % CF::A_ROW_CHUNKS) ^ swz_a(a_row0);
+    const uint32_t a_c0 = (lane % CF::A_ROW_CHUNKS) ^ swz_a<CF::MB>(a_row0);
     const uint32_t a_base = a_row0 * (uint32_t)K * 2u;
     const uint32_t b_k0 = wave * kBRowsPerLoad + lane / CF::B_ROW_CHUNKS;  // k row of load j = b_k0 + kBRowsPerJ j
     const uint32_t b_c0 = (lane % CF::B_ROW_CHUNKS) ^ swz_b(b_k0);
@@ -356,7 +389,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       if (j < CF::A_LOADS) {
         const uint32_t row = a_row0 + (uint32_t)(CF::A_RPL * CF::NW) * (uint32_t)j;
         // the swizzle of load j's row differs from a_row0's by a compile-time XOR
-        const uint32_t c = a_c0 ^ (swz_a((uint32_t)(CF::A_RPL * CF::NW * j)) ^ swz_a(0u));
+        const uint32_t c = a_c0 ^ (swz_a<CF::MB>((uint32_t)(CF::A_RPL * CF::NW * j)) ^ swz_a<CF::MB>(0u));
         const uint32_t vo = a_base + c * 16u + (uint32_t)(CF::A_RPL * CF::NW * j) * (uint32_t)K * 2u;
         const bool out = (int32_t)row >= m_left || (tail && k0 + (int32_t)(c * 8u) >= K);
         return out ? kBufOob : vo;
@@ -392,7 +425,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     for (int mi = 0; mi < CF::MI; ++mi) {
       const uint32_t row = wm * CF::WM + mi * CF::MB + (lane % CF::MB);
       off_a[mi] = row * (uint32_t)CF::A_ROW;
-      swa[mi] = swz_a(row) ^ (lane / CF::MB);
+      swa[mi] = swz_a<CF::MB>(row) ^ (lane / CF::MB);
     }
     uint32_t off_b[CF::NI];
     {
@@ -532,10 +565,16 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         read_frags(0, 0, a0, b0, 0, 0, 0);
         wait_lds_all();
         wg_barrier();  // stage 0 read by every wave before step kb's loads refill it
+        // claims are reserved now and sent from inside the step at claim_at
+        if (claim_at >= 0) reserve_claims();
+        uint32_t *claim_ctr = args.claim_policy == 0 ? &args.ctrl->counter : &args.ctrl->xcd_counter[region];
         auto step = [&](int32_t kt, const bf16x8(&ac)[CF::MI], const bf16x8(&bc)[CF::NI], bf16x8(&an)[CF::MI],
                         bf16x8(&bn)[CF::NI]) {
           const int st = (kt - kb) & 3;
-          if (kt == claim_at) do_claims();
+          if constexpr (MODE == kDynamic) {
+            claim_issue_asm(claim_ctr, kt == claim_at && batch_n >= 1u, batch[0]);
+            claim_issue_asm(claim_ctr, kt == claim_at && batch_n >= 2u, batch[1]);
+          }
           read_frags((st + 1) & 3, 0, an, bn, st, kt + 4, kLoads);
           mma(ac, bc);
           interleave<kReads, kMfma>();
@@ -562,6 +601,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // the epilogue: reading an atomic's answer waits for every older memory
     // operation of the wave, and the C stores would otherwise be among them.
     auto publish_claims = [&]() {
+      wait_vmem_all();  // the answers of claims sent from assembly
       for (uint32_t b = 0; b < batch_n; ++b) {
         const uint32_t v = claim_resolve(args, xcc, lane, b == 0 ? batch[0] : batch[1], region);
         const uint32_t ok = v < (uint32_t)T ? 1u : 0u;
