@@ -127,9 +127,9 @@ __device__ __forceinline__ void interleave() {
 //
 // A claim is split in two. claim_issue sends the first atomic (the global
 // counter, or the counter of the worker's current region: its own XCD's to
-// begin with) from lane 0 and returns its raw answer in lane 0's register
-// without waiting for it, so the round trip hides under the MFMAs of the
-// current tile. claim_resolve, called by a whole wave (all lanes active) once
+// begin with) from lane 0 and returns its raw answer in lane 0's register,
+// valid once the wave's memory operations have drained (vmcnt 0); the round
+// trip hides under the MFMAs of the current tile. claim_resolve, called by a whole wave (all lanes active) once
 // the answer is needed, broadcasts it and turns it into a tile id: every
 // decision is wave-uniform and the scheduler state lives in scalar registers.
 // Only when the current region is exhausted does it steal: it reads all eight
@@ -138,6 +138,28 @@ __device__ __forceinline__ void interleave() {
 // following claims are again a single hidden atomic. A claim that comes back
 // out of range proves that region exhausted for good (counters only grow), so
 // at most eight steal attempts are made.
+// The claim atomic as one assembly statement that skips itself unless `now`
+// (wave-uniform) is set: lane 0 alone adds 1 to *ctr (exec is narrowed inside
+// the statement) and receives the old value in `ret`. A main-loop step that
+// claims thus stays one basic block; a branch around the claim would split it,
+// and the register allocator then copies accumulators around the split. The
+// compiler does not see the atomic, so it never waits for it on its own (a
+// claim the compiler could see, on any path into the main loop, made it drain
+// every load at the loop head): readers of `ret` wait (vmcnt) explicitly.
+__device__ __forceinline__ void claim_issue_asm(uint32_t *ctr, bool now, uint32_t &ret) {
+  uint64_t saved;
+  asm volatile(
+      "s_cmp_eq_u32 %[now], 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "s_mov_b64 %[saved], exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %[ret], %[off], %[one], %[ctr] sc0\n\t"
+      "s_mov_b64 exec, %[saved]\n"
+      "1:"
+      : [ret] "+v"(ret), [saved] "=&s"(saved)
+      : [now] "s"(__builtin_amdgcn_readfirstlane(now ? 1u : 0u)), [off] "v"(0u), [one] "v"(1u), [ctr] "s"(ctr)
+      : "memory", "scc");
+}
 __device__ __forceinline__ uint32_t lane0_fetch_add(uint32_t *ctr, uint32_t lane) {
   uint32_t v = 0;
   if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -146,10 +168,10 @@ __device__ __forceinline__ uint32_t lane0_fetch_add(uint32_t *ctr, uint32_t lane
 __device__ __forceinline__ uint32_t region_size(uint32_t T, uint32_t y) {
   return T > y ? (T - y + kXcdRegions - 1) / kXcdRegions : 0u;
 }
-__device__ __forceinline__ uint32_t claim_issue(const KernelArgs &a, uint32_t region, uint32_t lane) {
+__device__ __forceinline__ uint32_t claim_issue(const KernelArgs &a, uint32_t region) {
   uint32_t *ctr = a.claim_policy == 0 ? &a.ctrl->counter : &a.ctrl->xcd_counter[region];
   uint32_t v = 0;
-  if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  claim_issue_asm(ctr, true, v);
   return v;
 }
 __device__ __forceinline__ uint32_t claim_resolve(const KernelArgs &a, uint32_t xcc, uint32_t lane, uint32_t raw,
@@ -178,29 +200,11 @@ __device__ __forceinline__ uint32_t claim_resolve(const KernelArgs &a, uint32_t 
   }
   return T;
 }
-// claim_issue's atomic as one assembly statement that skips itself unless
-// `now` (wave-uniform) is set: lane 0 alone adds 1 to *ctr (exec is narrowed
-// inside the statement) and receives the old value in `ret`. A main-loop step
-// that claims thus stays one basic block; a branch around the claim would split
-// it, and the register allocator then copies accumulators around the split. The
-// compiler does not see the atomic: the caller waits (vmcnt) before reading ret.
-__device__ __forceinline__ void claim_issue_asm(uint32_t *ctr, bool now, uint32_t &ret) {
-  uint64_t saved;
-  asm volatile(
-      "s_cmp_eq_u32 %[now], 0\n\t"
-      "s_cbranch_scc1 1f\n\t"
-      "s_mov_b64 %[saved], exec\n\t"
-      "s_mov_b64 exec, 1\n\t"
-      "global_atomic_add %[ret], %[off], %[one], %[ctr] sc0\n\t"
-      "s_mov_b64 exec, %[saved]\n"
-      "1:"
-      : [ret] "+v"(ret), [saved] "=&s"(saved)
-      : [now] "s"(__builtin_amdgcn_readfirstlane(now ? 1u : 0u)), [off] "v"(0u), [one] "v"(1u), [ctr] "s"(ctr)
-      : "memory", "scc");
-}
 
 __device__ __forceinline__ uint32_t claim_next(const KernelArgs &a, uint32_t xcc, uint32_t lane, uint32_t &region) {
-  return claim_resolve(a, xcc, lane, claim_issue(a, region, lane), region);
+  const uint32_t raw = claim_issue(a, region);
+  wait_vmem_all();
+  return claim_resolve(a, xcc, lane, raw, region);
 }
 
 template <int BM, int BN, int MODE, bool GROUPED>
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       if constexpr (MODE == kDynamic) {
         reserve_claims();
         for (uint32_t b = 0; b < batch_n; ++b) {
-          const uint32_t v = claim_issue(args, region, lane);
+          const uint32_t v = claim_issue(args, region);
           if (b == 0) batch[0] = v; else batch[1] = v;
         }
       }
@@ -568,6 +572,19 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         // claims are reserved now and sent from inside the step at claim_at
         if (claim_at >= 0) reserve_claims();
         uint32_t *claim_ctr = args.claim_policy == 0 ? &args.ctrl->counter : &args.ctrl->xcd_counter[region];
+        // The MFMA as a statement of its own, accumulating in place: each of the
+        // 64 accumulators keeps one AGPR quad for the whole loop (all 256 AGPRs
+        // hold accumulators, and with the builtin the register allocator
+        // rotated some through copies every trip). The statements are volatile
+        // and clobber memory, so program order is issue order: MFMA i, then
+        // fragment read i of the next k-step (24 reads), the loads spread
+        // between the reads. Hazards: within the loop the MFMA operands are
+        // written only by LDS reads (waited for), and accumulators are written
+        // only by MFMAs; the fences before and after the loop give the wait
+        // states the compiler cannot see.
+        auto mfma16 = [&](int mi, int ni, const bf16x8 &a, const bf16x8 &b) {
+          asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[mi][ni]) : "v"(b), "v"(a) : "memory");
+        };
         auto step = [&](int32_t kt, const bf16x8(&ac)[CF::MI], const bf16x8(&bc)[CF::NI], bf16x8(&an)[CF::MI],
                         bf16x8(&bn)[CF::NI]) {
           const int st = (kt - kb) & 3;
@@ -575,17 +592,50 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
             claim_issue_asm(claim_ctr, kt == claim_at && batch_n >= 1u, batch[0]);
             claim_issue_asm(claim_ctr, kt == claim_at && batch_n >= 2u, batch[1]);
           }
-          read_frags((st + 1) & 3, 0, an, bn, st, kt + 4, kLoads);
-          mma(ac, bc);
-          interleave<kReads, kMfma>();
-          // stage st+1 fully read and stage st+2 landed (the sixteen loads of the
-          // two steps since its own may still be in flight); the step's MFMAs
-          // are all issued first (no instruction moves across the fence)
-          __builtin_amdgcn_sched_barrier(0);
+          const int rst = (st + 1) & 3;
+          const unsigned char *sa = smem + rst * CF::STAGE;
+          const unsigned char *sb = sa + CF::A_STAGE;
+          const int32_t kt_load = kt + 4;
+          const i32x4 ra = make_rsrc_words(a_tile + kt_load * CF::BK, kt_load < ke);
+          const i32x4 rb = make_rsrc_words(b_tile + (size_t)(kt_load * CF::BK) * (size_t)N, kt_load < ke);
+          const uint32_t lbase = lds_addr(smem + st * CF::STAGE);
+          i16x4 lo[CF::NI];
+#pragma unroll
+          for (int i = 0; i < kMfma; ++i) {
+            mfma16(i / CF::NI, i % CF::NI, ac[i / CF::NI], bc[i % CF::NI]);
+            if (i < kReads) {
+              const int r = i;
+              if (r < CF::MI) {
+                an[r] = *(const bf16x8 *)(sa + off_a[r] + (swa[r] << 4));
+              } else {
+                const int ni = (r - CF::MI) >> 1;
+                const unsigned char *pb0 = sb + off_b[ni];
+                if (((r - CF::MI) & 1) == 0) {
+                  lo[ni] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0));
+                } else {
+                  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(pb0 + 4 * CF::B_ROW));
+                  typedef __attribute__((ext_vector_type(8))) short i16x8;
+                  const i16x8 v = __builtin_shufflevector(lo[ni], hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                  bn[ni] = __builtin_bit_cast(bf16x8, v);
+                }
+              }
+#pragma unroll
+              for (int j = 0; j < kLoads; ++j)
+                if (j * kReads / kLoads == r)
+                  load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
+            }
+          }
           wait_lds_all();
           asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
           wg_barrier();
         };
+        // the zeroed accumulators in their registers, then 16 wait states, before
+        // the first MFMA reads them
+#pragma unroll
+        for (int mi = 0; mi < CF::MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < CF::NI; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
         // two steps per trip, so the fragment buffers swap roles by name. An odd
         // count ends with one step past the unit: its stage was zero-filled, and
         // adding zero products leaves every accumulator bit for bit as it was.
@@ -593,6 +643,12 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
           step(kt, a0, b0, a1, b1);
           step(kt + 1, a1, b1, a0, b0);
         }
+        // 24 wait states after the last MFMA before anything reads an accumulator
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int mi = 0; mi < CF::MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < CF::NI; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
       }
     }
 
@@ -695,7 +751,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       if constexpr (MODE == kDynamic) {
         if (args.claims_ahead == 0 && !failed && last_sub) {
           batch_ord = next_ord;
-          batch[0] = claim_issue(args, region, lane);
+          batch[0] = claim_issue(args, region);
           batch_n = 1;
           ++next_ord;
           publish_claims();
