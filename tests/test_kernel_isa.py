@@ -1,0 +1,140 @@
+"""Checks on the compiled gfx950 code of the 256 x 256 main loop (CPU only: hipcc -S).
+
+The 16 x 16 main loop issues its MFMAs as assembly statements, so the compiler
+neither schedules them nor guards their hazards. These tests compile the kernel
+source to AMD assembly and check what that design relies on:
+
+- one basic block per trip of two k-steps, holding all 128 MFMAs, with no
+  accumulator copies and no scratch traffic;
+- no wait that drains every load (vmcnt(0)) inside the loop;
+- hazard distances: a VALU write of a register reaches an MFMA that reads it
+  only after many issue slots, and an MFMA result reaches any non-MFMA reader
+  only after at least the 19 wait states the longest MFMA needs.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(REPO, "persistent_tiled_gemm_amd", "csrc")
+HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None,
+                                reason="hipcc not installed")
+
+# enough for any MFMA result latency on this part (the 32-pass forms need 19)
+MIN_MFMA_RESULT_DISTANCE = 19
+# a VALU write feeding an MFMA operand needs a few wait states; demand far more
+MIN_VALU_TO_MFMA_DISTANCE = 16
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "gemm_kernel.s"
+    cmd = [HIPCC if os.path.exists(HIPCC) else "hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(REPO, "include"), "-I", CSRC, "--cuda-device-only", "-S",
+           "-o", str(out), os.path.join(CSRC, "gemm_kernel.hip")]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def kernel_lines(asm_text, mode, grouped):
+    name = f"_ZN3ptg15ptg_gemm_kernelILi256ELi256ELi{mode}ELb{1 if grouped else 0}EEEvNS_10KernelArgsE"
+    i = asm_text.index(name + ":")
+    j = asm_text.index(".Lfunc_end", i)
+    return asm_text[i:j]
+
+
+def instructions(block):
+    return [x.strip() for x in block.splitlines()
+            if x.strip() and not x.strip().startswith((";", ".")) and not x.strip().endswith(":")]
+
+
+def regs(operand):
+    operand = operand.strip().split()[0] if operand.strip() else ""
+    m = re.match(r"([va])\[(\d+):(\d+)\]", operand)
+    if m:
+        return {(m.group(1), k) for k in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", operand)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def operands(line):
+    return line.split(None, 1)[1].split(", ") if " " in line else []
+
+
+def slots(line):
+    op = line.split()[0]
+    return int(line.split()[1]) + 1 if op == "s_nop" else 1
+
+
+CASES = [(m, g) for m in (0, 1, 2) for g in (False, True)]
+
+
+@pytest.mark.parametrize("mode,grouped", CASES)
+def test_main_loop_is_one_block_without_copies(asm, mode, grouped):
+    text = kernel_lines(asm, mode, grouped)
+    blocks = re.split(r"\n\.LBB\d+_\d+:", text)
+    loops = [instructions(b) for b in blocks if sum(1 for x in instructions(b) if x.startswith("v_mfma_f32_16x16")) > 0]
+    assert len(loops) == 1, "the 16 x 16 MFMAs of a trip sit in more than one basic block"
+    body = loops[0]
+    assert sum(1 for x in body if x.startswith("v_mfma_f32_16x16x32_bf16")) == 128
+    assert not [x for x in body if x.startswith(("v_accvgpr_read", "v_accvgpr_write", "v_accvgpr_mov"))]
+    assert not [x for x in body if x.startswith("scratch_")]
+    assert not [x for x in body if x.startswith("s_waitcnt") and "vmcnt(0)" in x]
+    # four LDS stages: the end-of-step waits leave two steps of loads in flight
+    assert sum(1 for x in body if x.startswith("s_waitcnt") and "vmcnt(16)" in x) == 2
+    assert sum(1 for x in body if x.startswith("s_barrier")) == 2
+
+
+@pytest.mark.parametrize("mode,grouped", CASES)
+def test_mfma_hazard_distances(asm, mode, grouped):
+    f = instructions(kernel_lines(asm, mode, grouped))
+    mf = [n for n, x in enumerate(f) if x.startswith("v_mfma")]
+    # VALU write -> MFMA operand read, over the loop and its back edge
+    body = f[mf[0] - 64: mf[-1] + 32] * 2
+    last_valu, pos, worst = {}, 0, None
+    for x in body:
+        pos += slots(x)
+        op, ops = x.split()[0], operands(x)
+        if op.startswith("v_mfma"):
+            for r in ops[1:4]:
+                for reg in regs(r):
+                    if reg in last_valu:
+                        d = pos - last_valu[reg]
+                        worst = d if worst is None else min(worst, d)
+            for reg in regs(ops[0]):
+                last_valu.pop(reg, None)
+        elif op.startswith(("ds_read", "buffer_load", "global_load", "global_atomic")) and ops:
+            for reg in regs(ops[0]):
+                last_valu.pop(reg, None)
+        elif op.startswith("v_") and not op.startswith(("v_cmp", "v_readfirstlane", "v_readlane")) and ops:
+            for reg in regs(ops[0]):
+                last_valu[reg] = pos
+    assert worst is None or worst >= MIN_VALU_TO_MFMA_DISTANCE, worst
+    # MFMA result -> any other reader, from the loop to the end of the kernel
+    last_mfma, pos, worst = {}, 0, None
+    for x in f[mf[0]:]:
+        pos += slots(x)
+        op, ops = x.split()[0], operands(x)
+        if op.startswith("v_mfma"):
+            for reg in regs(ops[0]):
+                last_mfma[reg] = pos
+            continue
+        if op.startswith("s_") or not ops:
+            continue
+        store = op.startswith(("global_store", "buffer_store", "flat_store", "ds_write"))
+        for r in (ops if store else ops[1:]):
+            for reg in regs(r):
+                if reg in last_mfma:
+                    d = pos - last_mfma[reg]
+                    worst = d if worst is None else min(worst, d)
+        if not store:
+            for reg in regs(ops[0]):
+                last_mfma.pop(reg, None)
+    assert worst is None or worst >= MIN_MFMA_RESULT_DISTANCE, worst
