@@ -47,13 +47,16 @@ def test_partial_occupancy_against_model():
         span, t, ran = _span(ptg.gemm_read_log(plan), khz)
         sl = slog.cpu().numpy().reshape(64, 4).astype(np.float64)
         res[mode] = (span, t, (sl[:, 1].max() - ran["r0"].astype(np.float64).min()) / khz * 1e3)
-    t = res["static"][1]  # static's tiles all run on unshared CUs
-    tau = max(res["static"][2], 0.0) / t
-    avail = [0.0] * 192 + [tau] * 64
+    # each mode against the model fed with its own measured tile time t: under the
+    # spoiler the dynamic run's tiles take 7-25% longer than the static run's (a
+    # memory-system effect the model does not describe), so one t for both modes
+    # would put that difference on the scheduler
     for mode in ("static", "dynamic"):
+        span, t, spoiler_end = res[mode]
+        avail = [0.0] * 192 + [max(spoiler_end, 0.0) / t] * 64
         model = simulate([1.0] * 1024, mode, avail=avail, P=256).makespan
-        got = res[mode][0] / t
-        say(f"  {mode}: measured {got:.2f} t, model {model:.2f} t")
+        got = span / t
+        say(f"  {mode}: measured {got:.2f} t (t = {t:.1f} us), model {model:.2f} t")
         assert 0.8 * model <= got <= 1.25 * model, (mode, got, model)
     assert res["dynamic"][0] < res["static"][0]
     plan.destroy()
