@@ -256,7 +256,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--mode", default="dynamic", choices=["nonpersistent", "static", "dynamic"])
     ap.add_argument("--claims-ahead", type=int, default=1)
     ap.add_argument("--claim-policy", type=int, default=1, choices=[0, 1],
