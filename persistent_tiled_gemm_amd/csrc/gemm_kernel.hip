@@ -447,11 +447,11 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 
     // A fragment: 8 consecutive k of one row (ds_read_b128). B fragment: two
     // transposing reads of 4 k each (ds_read_b64_tr_b16) for one column. s
-    // selects the MFMA's k slice of the stage. Optionally, the loads of k-step
-    // kt_load into stage lst are placed in program order between the reads
-    // (32 x 32 blocks: load j after read j; 16 x 16: after read j * kReads /
-    // count, spread over the step's reads); the reads alternate
-    // with MFMAs, so the loads land between MFMAs instead of in one burst.
+    // selects the MFMA's k slice of the stage. Optionally (the 32 x 32 main
+    // loop), the loads of k-step kt_load into stage lst are placed in program
+    // order between the reads, load j after read j; the reads alternate with
+    // MFMAs, so the loads land between MFMAs instead of in one burst. (The
+    // 16 x 16 main loop places its reads and loads itself.)
     constexpr int kReads = CF::MI + 2 * CF::NI;
     auto read_frags = [&](int st, int s, bf16x8(&af)[CF::MI], bf16x8(&bfr)[CF::NI], int lst, int32_t kt_load,
                           int count) {
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         }
 #pragma unroll
         for (int j = 0; j < count; ++j)
-          if ((CF::MB == 32 ? j : j * kReads / count) == r)
+          if (j == r)
             load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
       }
     };
@@ -497,16 +497,16 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 #pragma unroll
         for (int e = 0; e < CF::ACC_N; ++e) acc[mi][ni][e] = 0.0f;
 
+    // the MFMAs of one 16-deep k slice, 32 x 32 blocks (the 16 x 16 main loop
+    // issues its own)
     auto mma = [&](const bf16x8(&af)[CF::MI], const bf16x8(&bfr)[CF::NI]) {
+      if constexpr (CF::MB == 32) {
 #pragma unroll
-      for (int mi = 0; mi < CF::MI; ++mi)
+        for (int mi = 0; mi < CF::MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < CF::NI; ++ni) {
-          if constexpr (CF::MB == 32)
+          for (int ni = 0; ni < CF::NI; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-          else
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-        }
+      }
     };
 
     // the prefetch claim is issued claim_lead k-steps before the tile ends (the
