@@ -140,12 +140,15 @@ __device__ __forceinline__ void interleave() {
 // at most eight steal attempts are made.
 // The claim atomic as one assembly statement that skips itself unless `now`
 // (wave-uniform) is set: lane 0 alone adds 1 to *ctr (exec is narrowed inside
-// the statement) and receives the old value in `ret`. A main-loop step that
-// claims thus stays one basic block; a branch around the claim would split it,
-// and the register allocator then copies accumulators around the split. The
-// compiler does not see the atomic, so it never waits for it on its own (a
-// claim the compiler could see, on any path into the main loop, made it drain
-// every load at the loop head): readers of `ret` wait (vmcnt) explicitly.
+// the statement) and receives the old value in `ret`. The compiler does not see
+// the atomic, so it never waits for it on its own (a claim the compiler could
+// see, on any path into the main loop, made it drain every load at the loop
+// head): readers of `ret` wait (vmcnt) explicitly. The 16 x 16 main loop sends
+// its claims from this statement between two runs of the same loop body, so
+// no k-step carries the claim's branch or EXEC write (either one inside the
+// step cost 70-90 cycles per step, measured: it holds the wave until the MFMAs
+// in flight drain) and no branch splits a step (the register allocator then
+// copies accumulators around the split).
 __device__ __forceinline__ void claim_issue_asm(uint32_t *ctr, bool now, uint32_t &ret) {
   uint64_t saved;
   asm volatile(
@@ -569,7 +572,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         read_frags(0, 0, a0, b0, 0, 0, 0);
         wait_lds_all();
         wg_barrier();  // stage 0 read by every wave before step kb's loads refill it
-        // claims are reserved now and sent from inside the step at claim_at
+        // claims are reserved now and sent between the two loop runs below
         if (claim_at >= 0) reserve_claims();
         uint32_t *claim_ctr = args.claim_policy == 0 ? &args.ctrl->counter : &args.ctrl->xcd_counter[region];
         // The MFMA as a statement of its own, accumulating in place: each of the
@@ -588,10 +591,6 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         auto step = [&](int32_t kt, const bf16x8(&ac)[CF::MI], const bf16x8(&bc)[CF::NI], bf16x8(&an)[CF::MI],
                         bf16x8(&bn)[CF::NI]) {
           const int st = (kt - kb) & 3;
-          if constexpr (MODE == kDynamic) {
-            claim_issue_asm(claim_ctr, kt == claim_at && batch_n >= 1u, batch[0]);
-            claim_issue_asm(claim_ctr, kt == claim_at && batch_n >= 2u, batch[1]);
-          }
           const int rst = (st + 1) & 3;
           const unsigned char *sa = smem + rst * CF::STAGE;
           const unsigned char *sb = sa + CF::A_STAGE;
@@ -639,7 +638,19 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         // two steps per trip, so the fragment buffers swap roles by name. An odd
         // count ends with one step past the unit: its stage was zero-filled, and
         // adding zero products leaves every accumulator bit for bit as it was.
-        for (int32_t kt = kb; kt < ke; kt += 2) {
+        // The dynamic scheduler runs the loop in two parts and sends its claims
+        // between them, at the trip boundary at or before claim_at.
+        int32_t kt = kb;
+        if constexpr (MODE == kDynamic) {
+          const int32_t split_at = claim_at >= kb ? kb + ((claim_at - kb) & ~1) : ke;
+          for (; kt < split_at; kt += 2) {
+            step(kt, a0, b0, a1, b1);
+            step(kt + 1, a1, b1, a0, b0);
+          }
+          claim_issue_asm(claim_ctr, batch_n >= 1u, batch[0]);
+          claim_issue_asm(claim_ctr, batch_n >= 2u, batch[1]);
+        }
+        for (; kt < ke; kt += 2) {
           step(kt, a0, b0, a1, b1);
           step(kt + 1, a1, b1, a0, b0);
         }
@@ -665,8 +676,19 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         if (lane == 0) ring[(batch_ord + b) % (uint32_t)args.ring_depth] = RingRec{v, ok, batch_ord + b, 0u};
       }
     };
+    // With claims sent during the unit, the next unit's record is read right
+    // after they are published, so the end of the unit needs no barrier.
+    RingRec next_rec = RingRec{0u, 0u, 0u, 0u};
+    bool next_read = false;
     if constexpr (MODE == kDynamic) {
-      if (wave == 0 && args.claims_ahead >= 1) publish_claims();
+      if (args.claims_ahead >= 1) {
+        if (wave == 0) publish_claims();
+        if (last_sub) {
+          __syncthreads();
+          next_rec = ring[(ord + 1) % (uint32_t)args.ring_depth];
+          next_read = true;
+        }
+      }
     }
 
     // ---- epilogue: fp32 accumulators -> C. Lane l holds, in each group of four
@@ -791,8 +813,11 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     }
     sub = 0;
     if constexpr (MODE == kDynamic) {
-      __syncthreads();
-      const RingRec rec = ring[(ord + 1) % (uint32_t)args.ring_depth];
+      if (!next_read) {
+        __syncthreads();
+        next_rec = ring[(ord + 1) % (uint32_t)args.ring_depth];
+      }
+      const RingRec rec = next_rec;
       const uint32_t seq = wave_uniform(rec.seq);
       valid = wave_uniform(rec.valid) != 0;
       unit = wave_uniform(rec.tile);

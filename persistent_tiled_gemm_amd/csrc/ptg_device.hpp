@@ -64,17 +64,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 
 // 16 bytes per lane from global memory straight into LDS at lds_base + lane*16
-// (lds_base is wave-uniform; it goes to M0). Issued as inline assembly so the
-// compiler does not add a conservative wait before every later LDS read: the
-// kernel waits for these loads itself (vmcnt) before the barrier that
-// publishes the stage.
+// (lds_base is wave-uniform; the instruction takes it from M0, which the
+// statement names as an input so that the compiler itself sets M0 and knows the
+// statement reads it). Issued as inline assembly so the compiler does not add a
+// conservative wait before every later LDS read: the kernel waits for these
+// loads itself (vmcnt) before the barrier that publishes the stage.
 __device__ __forceinline__ void load16_to_lds(i32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %0, %2, 0 offen lds"
-      :
-      : "v"(voffset), "s"(lds_base), "s"(rsrc)
-      : "memory", "m0");
+  asm volatile("buffer_load_dwordx4 %0, %2, 0 offen lds"
+               :
+               : "v"(voffset), "{m0}"(lds_base), "s"(rsrc)
+               : "memory");
 }
 
 __device__ __forceinline__ void wait_lds_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
