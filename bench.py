@@ -76,6 +76,18 @@ def time_runs(fn, steps: int, warmup: int, stream):
     return start.elapsed_time(end) / steps  # ms per step
 
 
+def time_interleaved(fns, rounds: int, per_round: int, stream):
+    """Mean ms per call of each function, timed in `rounds` blocks of `per_round` calls per function,
+    the order of the functions alternating between rounds; each block starts with three untimed calls
+    (the first call after a switch or an idle gap reads slow)."""
+    total = {k: 0.0 for k in fns}
+    names = list(fns)
+    for r in range(rounds):
+        for k in (names if r % 2 == 0 else names[::-1]):
+            total[k] += time_runs(fns[k], per_round, 3, stream) * per_round
+    return {k: total[k] / (rounds * per_round) for k in names}
+
+
 def cu_key(hw_id, xcc_id):
     """Physical CU identity from the HW_ID register (cu, sh, se fields, bits 8..15) and the XCC id."""
     return (xcc_id.astype(np.int64) << 8) | ((hw_id.astype(np.int64) >> 8) & 0xFF)
@@ -345,22 +357,31 @@ def main():
         runs = [("nonpersistent", "nonpersistent", plan), ("static", "static", plan), ("dynamic", "dynamic", plan),
                 ("dynamic_single_counter" if args.claim_policy == 1 else "dynamic_xcd_counters", "dynamic", plan_other),
                 ("dynamic_claim_groups_2x2", "dynamic", plan_group)]
-        for name, mode, pl in runs:
-            m_ms = time_runs(lambda: ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream), max(5, args.steps // 2),
-                             2, stream)
-            ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream)
-            mk = makespan_from_log(ptg.gemm_read_log(pl), khz) if not args.no_log else None
+        fns = {name: (lambda mode=mode, pl=pl: ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream))
+               for name, mode, pl in runs}
+        # context only: the vendor library's bf16 GEMM at the same shape (torch.matmul -> hipBLASLt), which
+        # writes a bf16 C (half of our fp32 C bytes), and, where torch offers it, the same product with an
+        # fp32 C (torch.mm with out_dtype), the exact counterpart of this kernel
+        fns["vendor_matmul_bf16_out"] = lambda: torch.matmul(A, B)
+        try:
+            torch.mm(A, B, out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            fns["vendor_mm_fp32_out"] = lambda: torch.mm(A, B, out_dtype=torch.float32)
+        except (RuntimeError, TypeError) as e:  # not offered by this build: reported as absent
+            log(f"vendor fp32-output mm unavailable: {e}")
+        # the clock drifts over tens of milliseconds under this load, so the variants are timed in
+        # interleaved blocks (alternating order), not one after another
+        per_mode = time_interleaved(fns, rounds=4, per_round=max(5, args.steps // 5), stream=stream)
+        for name, m_ms in per_mode.items():
             modes[name] = {"ms": m_ms, "tflops": flops / (m_ms * 1e-3) / 1e12,
                            "frac_peak": flops / (m_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        for name, mode, pl in runs:
+            ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream)
+            mk = makespan_from_log(ptg.gemm_read_log(pl), khz) if not args.no_log else None
             if mk:
                 modes[name].update(makespan_us=mk["makespan_us"], tile_median_us=mk["tile_median_us"])
         plan_other.destroy()
         plan_group.destroy()
-        # context only: the vendor library's bf16 GEMM at the same shape (torch.matmul -> hipBLASLt). It
-        # writes a bf16 C (half of our fp32 C bytes), so it is a near, not an exact, comparison.
-        v_ms = time_runs(lambda: torch.matmul(A, B), max(5, args.steps // 2), 2, stream)
-        modes["vendor_matmul_bf16_out"] = {"ms": v_ms, "tflops": flops / (v_ms * 1e-3) / 1e12,
-                                           "frac_peak": flops / (v_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
     roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(1.0),
