@@ -235,3 +235,30 @@ def test_xcd_regions_drained_by_stealing(shape, cap):
     log = check_log(plan, "dynamic", T)
     assert len(np.unique(log["worker"])) <= T
     plan.destroy()
+
+
+@pytest.mark.parametrize("K", [32, 96, 320, 1000])
+@pytest.mark.parametrize("q", [1, 2])
+def test_claim_point_anywhere_in_the_tile(K, q):
+    # The dynamic 256 x 256 main loop runs in two parts and sends its claims at the two-step trip
+    # boundary at or before k-step nk - claim_lead: leads of 0 (last pair), 1, 2, 3 and past the
+    # tile start, odd and even k-step counts (nk = 1, 3, 10, 32 with a K tail), one or two claims
+    # ahead. Three workers at most, so each takes many tiles and every claim point recurs. The
+    # result must equal the static run's bit for bit, and the log must be exactly-once.
+    p = make_problem(1280, 1024, K, "uniform", seed=K + q)  # 5 x 4 tiles of 256
+    T = 20
+    plain = make_plan(256)
+    say(f"case claim point K={K} claims_ahead={q}: static reference")
+    ref = run(p, plain, "static")
+    assert_close_full(p, ref)
+    plain.destroy()
+    for lead in (0, 1, 2, 3, 1000):
+        for policy in (0, 1):
+            plan = make_plan(256, claims_ahead=q, claim_lead=lead, claim_policy=policy, max_concurrent=3,
+                             min_lds_bytes=96 * 1024)
+            say(f"case claim point K={K} claims_ahead={q} lead={lead} policy={policy}")
+            c = run(p, plan, "dynamic")
+            assert np.array_equal(c, ref)
+            log = check_log(plan, "dynamic", T, K=K)
+            assert len(np.unique(log["worker"])) <= T
+            plan.destroy()
