@@ -402,9 +402,14 @@ def main():
     # context for the roofline: the MFMA-only rate and clock with random operands (no memory traffic),
     # the ceiling the power limit leaves any bf16 GEMM on this part
     if not args.no_modes:
-        ptg.gemm_mfma_probe(iters=40000, random_operands=True)  # warm-up: the clock settles
-        out["mfma_ceiling"] = dict(ptg.gemm_mfma_probe(iters=40000, random_operands=True),
-                                   what="MFMA-only kernel, random bf16 operands, all CUs, second of two runs")
+        # the kernel's own instruction (16 x 16 x 32) first, then the 32 x 32 x 16 form for comparison
+        ptg.gemm_mfma_probe(iters=40000, random_operands=True, mfma_block=16)  # warm-up: the clock settles
+        out["mfma_ceiling"] = dict(ptg.gemm_mfma_probe(iters=40000, random_operands=True, mfma_block=16),
+                                   what="MFMA-only kernel of v_mfma_f32_16x16x32_bf16 (the 256 x 256 tiles' "
+                                        "instruction), random bf16 operands, all CUs, second of two runs")
+        out["mfma_ceiling"]["tflops_frac_achieved"] = tflops / out["mfma_ceiling"]["tflops"]
+        ptg.gemm_mfma_probe(iters=40000, random_operands=True, mfma_block=32)
+        out["mfma_ceiling"]["mfma_32x32x16"] = ptg.gemm_mfma_probe(iters=40000, random_operands=True, mfma_block=32)
     if not args.no_tail:
         out["tail"] = run_tail_sections(ptg, torch, stream, khz, (p, A, B, C))
     plan.destroy()

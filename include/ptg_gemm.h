@@ -279,16 +279,19 @@ gemm_status gemm_spoiler_run(int32_t device, int32_t n_wgs, int64_t spin_ns, voi
 /*
  * Measurement helper (no page behind it; a fact about the part): run an
  * MFMA-only kernel on `device`, one workgroup of four waves per CU, each wave
- * issuing `iters` rounds of eight independent v_mfma_f32_32x32x16_bf16 with no
- * memory traffic, operands constant (random_operands == 0) or changing from
- * one MFMA to the next (pseudo-random bf16). Synchronous: it allocates a small
- * scratch buffer, times the launch with events and frees the buffer. Outputs:
- * *tflops_out, the dense bf16 rate achieved, and *clock_ghz_out, the mean
- * shader clock during the run (s_memtime over s_memrealtime ticks). iters must
- * be in 1..10^7.
+ * issuing `iters` rounds of independent bf16 MFMAs with no memory traffic:
+ * eight v_mfma_f32_32x32x16_bf16 (mfma_block == 32, the 128 x 128 tiles'
+ * instruction) or sixteen v_mfma_f32_16x16x32_bf16 (mfma_block == 16, the
+ * 256 x 256 tiles' instruction) per round, the same flops either way; operands
+ * constant (random_operands == 0) or differing from one MFMA to the next
+ * (pseudo-random bf16). Synchronous: it allocates a small scratch buffer, times
+ * the launch with events and frees the buffer. Outputs: *tflops_out, the dense
+ * bf16 rate achieved, and *clock_ghz_out, the mean shader clock during the run
+ * (s_memtime over s_memrealtime ticks). iters must be in 1..10^7 and
+ * mfma_block 16 or 32, else GEMM_E_INVALID_ARG.
  */
-gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operands, double *tflops_out,
-                            double *clock_ghz_out);
+gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operands, int32_t mfma_block,
+                            double *tflops_out, double *clock_ghz_out);
 
 #ifdef __cplusplus
 }

@@ -114,7 +114,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gemm_last_hip_error.restype = ctypes.c_char_p
     lib.gemm_test_preset_counter.argtypes = [vp, u32]
     lib.gemm_spoiler_run.argtypes = [i32, i32, i64, vp, vp, ctypes.c_double]
-    lib.gemm_mfma_probe.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.gemm_mfma_probe.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double)]
     for name in ABI_FUNCTIONS:
         if name not in ("gemm_status_str", "gemm_last_hip_error"):
             getattr(lib, name).restype = ctypes.c_int32
@@ -303,12 +304,13 @@ def gemm_spoiler_run(n_wgs: int, spin_ns: int, stream=None, log=None, wait_resid
     _check(st, "gemm_spoiler_run")
 
 
-def gemm_mfma_probe(iters: int = 20000, random_operands: bool = True, device: int = 0) -> dict:
-    """gemm_mfma_probe: MFMA-only bf16 rate and shader clock on every CU (no memory traffic)."""
+def gemm_mfma_probe(iters: int = 20000, random_operands: bool = True, mfma_block: int = 16, device: int = 0) -> dict:
+    """gemm_mfma_probe: MFMA-only bf16 rate and shader clock on every CU (no memory traffic), with
+    16 x 16 x 32 (mfma_block=16) or 32 x 32 x 16 (mfma_block=32) MFMAs."""
     tf = ctypes.c_double(0.0)
     ghz = ctypes.c_double(0.0)
-    st = load_library().gemm_mfma_probe(int(device), int(iters), 1 if random_operands else 0, ctypes.byref(tf),
-                                        ctypes.byref(ghz))
+    st = load_library().gemm_mfma_probe(int(device), int(iters), 1 if random_operands else 0, int(mfma_block),
+                                        ctypes.byref(tf), ctypes.byref(ghz))
     _check(st, "gemm_mfma_probe")
     return {"tflops": tf.value, "clock_ghz": ghz.value}
 

@@ -591,9 +591,10 @@ gemm_status gemm_spoiler_run(int32_t device, int32_t n_wgs, int64_t spin_ns, voi
   return GEMM_OK;
 }
 
-gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operands, double *tflops_out,
-                            double *clock_ghz_out) {
+gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operands, int32_t mfma_block,
+                            double *tflops_out, double *clock_ghz_out) {
   if (!tflops_out || !clock_ghz_out || iters < 1 || iters > 10000000) return GEMM_E_INVALID_ARG;
+  if (mfma_block != 16 && mfma_block != 32) return GEMM_E_INVALID_ARG;
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return GEMM_E_HIP;
   if (cur != device) return GEMM_E_DEVICE;
@@ -612,7 +613,7 @@ gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operan
     st = GEMM_E_NOMEM;
   } else if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess ||
              hipEventRecord(e0, nullptr) != hipSuccess ||
-             ptg::launch_mfma_probe(grid, iters, random_operands != 0, sink, ticks, nullptr) != hipSuccess ||
+             ptg::launch_mfma_probe(grid, iters, random_operands != 0, mfma_block, sink, ticks, nullptr) != hipSuccess ||
              hipEventRecord(e1, nullptr) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
              hipEventElapsedTime(&ms, e0, e1) != hipSuccess ||
              hipMemcpy(h.data(), ticks, sizeof(uint64_t) * h.size(), hipMemcpyDeviceToHost) != hipSuccess) {
@@ -626,8 +627,8 @@ gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operan
       double ratio = 0.0;
       for (int i = 0; i < grid; ++i) ratio += (double)h[2 * i] / (double)std::max<uint64_t>(h[2 * i + 1], 1);
       ratio /= grid;
-      // 4 waves x 8 MFMAs x 32*32*16*2 flop per round and workgroup
-      const double flops = 4.0 * 8.0 * 32768.0 * (double)iters * (double)grid;
+      // 4 waves x (8 MFMAs of 32*32*16*2 or 16 of 16*16*32*2) flop per round and workgroup
+      const double flops = 4.0 * 262144.0 * (double)iters * (double)grid;
       *tflops_out = flops / ((double)ms * 1e-3) / 1e12;
       *clock_ghz_out = ratio * (double)wclk * 1e-6;
     }

@@ -89,9 +89,10 @@ int gemm_static_lds_bytes(int tile_edge);
 
 hipError_t launch_spoiler(int n_wgs, uint64_t spin_ticks, uint32_t *resident, uint64_t *log, hipStream_t stream);
 
-// MFMA-only probe: `grid` workgroups of four waves, `iters` rounds of eight
-// 32x32x16 bf16 MFMAs per wave; ticks receives {s_memtime, s_memrealtime}
-// deltas per workgroup.
-hipError_t launch_mfma_probe(int grid, int32_t iters, bool vary, float *sink, uint64_t *ticks, hipStream_t s);
+// MFMA-only probe: `grid` workgroups of four waves, `iters` rounds per wave of
+// eight 32x32x16 (mfma_block 32) or sixteen 16x16x32 (mfma_block 16) bf16
+// MFMAs; ticks receives {s_memtime, s_memrealtime} deltas per workgroup.
+hipError_t launch_mfma_probe(int grid, int32_t iters, bool vary, int mfma_block, float *sink, uint64_t *ticks,
+                             hipStream_t s);
 
 }  // namespace ptg
