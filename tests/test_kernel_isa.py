@@ -81,8 +81,9 @@ def test_main_loop_is_one_block_without_copies(asm, mode, grouped):
     text = kernel_lines(asm, mode, grouped)
     blocks = re.split(r"\n\.LBB\d+_\d+:", text)
     loops = [instructions(b) for b in blocks if sum(1 for x in instructions(b) if x.startswith("v_mfma_f32_16x16")) > 0]
-    # the dynamic scheduler runs the same loop body twice and claims in between
-    assert len(loops) == (2 if mode == 2 else 1), "the 16 x 16 MFMAs of a trip sit in more than one basic block"
+    # each run of the loop has a fast form (load offsets computed once per tile) and a K-tail form;
+    # the dynamic scheduler runs the loop in two parts and claims in between
+    assert len(loops) == (4 if mode == 2 else 2), "the 16 x 16 MFMAs of a trip sit in more than one basic block"
     for body in loops:
         assert sum(1 for x in body if x.startswith("v_mfma_f32_16x16x32_bf16")) == 128
         assert not [x for x in body if x.startswith(("v_accvgpr_read", "v_accvgpr_write", "v_accvgpr_mov"))]
@@ -102,7 +103,7 @@ def test_main_loop_has_no_claim_branch_or_exec_write(asm, mode, grouped):
     # split at every label, the assembly statements' local labels included
     blocks = re.split(r"\n(?:\.LBB\d+_\d+|\d+):", text)
     loops = [instructions(b) for b in blocks if sum(1 for x in instructions(b) if x.startswith("v_mfma_f32_16x16")) > 0]
-    assert len(loops) == (2 if mode == 2 else 1)
+    assert len(loops) == (4 if mode == 2 else 2)
     for body in loops:
         # the trip ends at its back edge (the block's text may run on past it)
         ends = [n for n, x in enumerate(body) if x.startswith(("s_cbranch", "s_branch", "s_setpc"))]
@@ -159,3 +160,21 @@ def test_mfma_hazard_distances(asm, mode, grouped):
             for reg in regs(ops[0]):
                 last_mfma.pop(reg, None)
     assert worst is None or worst >= MIN_MFMA_RESULT_DISTANCE, worst
+
+
+@pytest.mark.parametrize("mode,grouped", CASES)
+def test_fast_trips_compute_no_load_masks(asm, mode, grouped):
+    """Vector instructions interleaved with the MFMAs stall them (recomputing the load masks every
+    k-step cost about 220 cycles per step), so half of the trips, those with no partial K, carry
+    only the LDS read address adds: at most 24 non-MFMA vector instructions per trip of two
+    k-steps (the K-tail trips carry about 65)."""
+    text = kernel_lines(asm, mode, grouped)
+    blocks = re.split(r"\n\.LBB\d+_\d+:", text)
+    loops = [instructions(b) for b in blocks if sum(1 for x in instructions(b) if x.startswith("v_mfma_f32_16x16")) > 0]
+    valu = []
+    for body in loops:
+        ends = [n for n, x in enumerate(body) if x.startswith(("s_cbranch", "s_branch"))]
+        body = body[: ends[0] + 1]
+        valu.append(sum(1 for x in body if x.startswith("v_") and not x.startswith("v_mfma")))
+    fast = [v for v in valu if v <= 24]
+    assert len(fast) == len(loops) // 2, valu
