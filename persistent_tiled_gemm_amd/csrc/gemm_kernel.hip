@@ -388,43 +388,37 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     const int32_t kb = split ? (int32_t)((uint32_t)nk * chunk / (uint32_t)args.split_chunks) : 0;
     const int32_t ke = split ? (int32_t)((uint32_t)nk * (chunk + 1u) / (uint32_t)args.split_chunks) : nk;
 
-    // voffset of load j (A loads first, then B) for k-step kt; chunks outside
-    // the matrix (row / column edges, K tail) read as zero via kBufOob. Every
-    // chunk of a k-step past the unit's end reads as zero through its resource
-    // (record count 0).
-    auto load_voff = [&](int j, int32_t kt) -> uint32_t {
-      const int32_t k0 = kt * CF::BK;
-      const bool tail = kt >= full;
-      if (j < CF::A_LOADS) {
-        const uint32_t row = a_row0 + (uint32_t)(CF::A_RPL * CF::NW) * (uint32_t)j;
-        // the swizzle of load j's row differs from a_row0's by a compile-time XOR
-        const uint32_t c = a_c0 ^ (swz_a<CF::MB>((uint32_t)(CF::A_RPL * CF::NW * j)) ^ swz_a<CF::MB>(0u));
-        const uint32_t vo = a_base + c * 16u + (uint32_t)(CF::A_RPL * CF::NW * j) * (uint32_t)K * 2u;
-        const bool out = (int32_t)row >= m_left || (tail && k0 + (int32_t)(c * 8u) >= K);
-        return out ? kBufOob : vo;
-      }
-      const int jb = j - CF::A_LOADS;
-      const uint32_t krow = b_k0 + kBRowsPerJ * (uint32_t)jb;
-      const uint32_t bb = ((kBRowsPerJ * (uint32_t)jb) & 8u) ? b_base1 : b_base0;
-      const uint32_t vo = bb + (uint32_t)jb * kBRowsPerJ * (uint32_t)N * 2u;
-      const bool out = bb == kBufOob || (tail && k0 + (int32_t)krow >= K);
-      return out ? kBufOob : vo;
+    // voffset of load j of a k-step with no partial K: chunks outside the matrix
+    // (row / column edges) read as zero via kBufOob. The A swizzle of load j's
+    // row differs from a_row0's by a compile-time XOR; B has two per-lane bases.
+    auto load_chunk_a = [&](int j) -> uint32_t {
+      return a_c0 ^ (swz_a<CF::MB>((uint32_t)(CF::A_RPL * CF::NW * j)) ^ swz_a<CF::MB>(0u));
     };
-    // the same without the K-tail test: what a k-step with no partial K reads
-    // (edge rows / columns still read as zero). Loop-invariant, so the 16 x 16
-    // main loop computes it once per tile: recomputing the masks every k-step
-    // cost about 220 cycles per step in vector instructions interleaved with
-    // the MFMAs (measured: 406k -> 350k cycles per 8192^3 tile).
     auto load_voff_edge = [&](int j) -> uint32_t {
       if (j < CF::A_LOADS) {
         const uint32_t row = a_row0 + (uint32_t)(CF::A_RPL * CF::NW) * (uint32_t)j;
-        const uint32_t c = a_c0 ^ (swz_a<CF::MB>((uint32_t)(CF::A_RPL * CF::NW * j)) ^ swz_a<CF::MB>(0u));
-        const uint32_t vo = a_base + c * 16u + (uint32_t)(CF::A_RPL * CF::NW * j) * (uint32_t)K * 2u;
+        const uint32_t vo = a_base + load_chunk_a(j) * 16u + (uint32_t)(CF::A_RPL * CF::NW * j) * (uint32_t)K * 2u;
         return (int32_t)row >= m_left ? kBufOob : vo;
       }
       const int jb = j - CF::A_LOADS;
       const uint32_t bb = ((kBRowsPerJ * (uint32_t)jb) & 8u) ? b_base1 : b_base0;
       return bb == kBufOob ? kBufOob : bb + (uint32_t)jb * kBRowsPerJ * (uint32_t)N * 2u;
+    };
+    // voffset of load j (A loads first, then B) for k-step kt: the same, and in
+    // the partial k-step (K tail) chunks past K read as zero too. Every chunk of
+    // a k-step past the unit's end reads as zero through its resource (record
+    // count 0). The edge offsets do not depend on kt, so the 16 x 16 main loop
+    // computes them once per tile and uses them in every trip with no partial
+    // K: recomputing the masks every k-step cost about 220 cycles per step in
+    // vector instructions interleaved with the MFMAs (measured: 406k -> 350k
+    // cycles per 8192^3 tile).
+    auto load_voff = [&](int j, int32_t kt) -> uint32_t {
+      const uint32_t vo = load_voff_edge(j);
+      if (kt < full) return vo;
+      const int32_t k0 = kt * CF::BK;
+      const int32_t kfirst = j < CF::A_LOADS ? k0 + (int32_t)(load_chunk_a(j) * 8u)
+                                             : k0 + (int32_t)(b_k0 + kBRowsPerJ * (uint32_t)(j - CF::A_LOADS));
+      return kfirst >= K ? kBufOob : vo;
     };
     auto load_dst = [&](int j) -> uint32_t {
       return j < CF::A_LOADS ? (uint32_t)(j * CF::NW + (int)wave) * 1024u
