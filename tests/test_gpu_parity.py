@@ -262,3 +262,24 @@ def test_claim_point_anywhere_in_the_tile(K, q):
             log = check_log(plan, "dynamic", T, K=K)
             assert len(np.unique(log["worker"])) <= T
             plan.destroy()
+
+
+@pytest.mark.parametrize("K", [8, 40, 136, 200, 232, 264, 488, 1000, 1240])
+def test_k_tail_on_every_trip_boundary(K):
+    # The 256 x 256 main loop uses load offsets computed once per tile for trips whose loads read whole
+    # 32-deep slices, and recomputes them with the K-tail test from the first trip whose loads reach
+    # the partial k-step. These K put that trip at every position: all trips (K = 8, 40, 136), from
+    # the second trip (200, 232), later (264, 488, 1000, 1240), with odd and even k-step counts.
+    p = make_problem(520, 776, K, "uniform", seed=K)  # 3 x 4 tiles of 256, ragged in M and N
+    plan = make_plan(256)
+    outs = {}
+    for mode in MODES:
+        say(f"case k tail K={K} mode={mode}")
+        c = run(p, plan, mode)
+        assert_close_full(p, c)
+        info = ptg.gemm_plan_info_get(plan)
+        check_log(plan, mode, 12, P=info["last_grid"] if mode == "static" else None, K=K)
+        outs[mode] = c
+    assert np.array_equal(outs["static"], outs["dynamic"])
+    assert np.array_equal(outs["nonpersistent"], outs["dynamic"])
+    plan.destroy()
