@@ -105,6 +105,22 @@ def makespan_from_log(rec, khz):
             "workers": int(len(np.unique(ran["worker"]))), "cus": int(len(np.unique(cu_key(ran["hw_id"], ran["xcc_id"]))))}
 
 
+def median_run(run_and_read, khz, n: int = 3):
+    """Call run_and_read() n times (it runs one launch, waits for it and returns (log records, extra
+    fields)); return the makespan summary of the run with the median makespan, with every run's
+    makespan listed."""
+    runs = []
+    for _ in range(n):
+        rec, extra = run_and_read()
+        ms = makespan_from_log(rec, khz)
+        ms.update(extra)
+        runs.append((ms["makespan_us"], ms, rec))
+    runs.sort(key=lambda x: x[0])
+    _, ms, rec = runs[len(runs) // 2]
+    ms["makespan_us_runs"] = [round(x[0], 2) for x in runs]
+    return ms, rec
+
+
 def cpu_baseline(problem, target_s: float = 10.0):
     """Time the CPU oracle (gemm_ref_rows: exact bf16 decode + fp64 product) on a row sample."""
     from oracle.gemm_ref import gemm_ref_rows
@@ -140,20 +156,20 @@ def run_tail_sections(ptg, torch, stream, khz, square):
     plan = ptg.gemm_create(tile_edge=256, log_capacity=1024)
     spoil_stream = torch.cuda.Stream()
     res = {}
-    for mode in modes:
-        ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)  # warm
-        torch.cuda.synchronize()
+    def co_run(mode):
         spoiler_log = torch.zeros(64 * 4, dtype=torch.int64, device="cuda")
         ptg.gemm_spoiler_run(64, 2_000_000, stream=spoil_stream, log=spoiler_log, wait_resident_ms=2000.0)
         ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
         torch.cuda.synchronize()
         rec = ptg.gemm_read_log(plan)
-        ms = makespan_from_log(rec, khz)
         sl = spoiler_log.cpu().numpy().reshape(64, 4).astype(np.float64)
-        ms["spoiler_cus"] = int(len(np.unique(cu_key(sl[:, 2].astype(np.int64), sl[:, 3].astype(np.int64)))))
         ran = rec[rec["visits"] > 0]
-        ms["spoiler_end_after_first_tile_us"] = float((sl[:, 1].max() - ran["r0"].min()) / khz * 1e3)
-        res[mode] = ms
+        return rec, {"spoiler_cus": int(len(np.unique(cu_key(sl[:, 2].astype(np.int64), sl[:, 3].astype(np.int64))))),
+                     "spoiler_end_after_first_tile_us": float((sl[:, 1].max() - ran["r0"].min()) / khz * 1e3)}
+    for mode in modes:
+        ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)  # warm
+        torch.cuda.synchronize()
+        res[mode], _ = median_run(lambda: co_run(mode), khz)
     # each mode in its own median tile time (under the spoiler the dynamic run's
     # tiles take longer than the static run's, a memory effect, not scheduling)
     for mode in modes:
@@ -171,31 +187,29 @@ def run_tail_sections(ptg, torch, stream, khz, square):
     plan = ptg.gemm_create(tile_edge=256, log_capacity=1024)
     res = {}
     ks = np.array([q.K for q in w.problems])
-    for mode in modes:
-        ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode, stream=stream)
+    # the dynamic scheduler handing out the longest-K problems first, beside the three modes
+    lplan = ptg.gemm_create(tile_edge=256, log_capacity=1024, group_order=1)
+    variants = {mode: (mode, plan) for mode in modes}
+    variants["dynamic_longest_k_first"] = ("dynamic", lplan)
+    fns = {name: (lambda mode=mode, pl=pl: ptg.gemm_run_grouped(As, Bs, Cs, pl, mode=mode, stream=stream))
+           for name, (mode, pl) in variants.items()}
+    kernel_ms = time_interleaved(fns, rounds=4, per_round=5, stream=stream)
+
+    def logged(fn, pl):
+        fn()
         torch.cuda.synchronize()
-        ms_ev = time_runs(lambda: ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode, stream=stream), 5, 1, stream)
-        ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode, stream=stream)
-        rec = ptg.gemm_read_log(plan)
-        ms = makespan_from_log(rec, khz)
-        ms["kernel_ms"] = ms_ev
-        ms["tflops"] = w.flops / (ms_ev * 1e-3) / 1e12
-        res[mode] = ms
-        if mode == "static":
+        return ptg.gemm_read_log(pl), {}
+    for name, (mode, pl) in variants.items():
+        ms, rec = median_run(lambda: logged(fns[name], pl), khz)
+        ms["kernel_ms"] = kernel_ms[name]
+        ms["tflops"] = w.flops / (kernel_ms[name] * 1e-3) / 1e12
+        res[name] = ms
+        if name == "static":
             ran = rec[rec["visits"] > 0]
             dur = ((ran["r1"] - ran["r0"]).astype(np.float64) / khz * 1e3)
             kt = ks[ran["problem"]] / 64.0
             alpha, beta = np.polyfit(kt, dur, 1)
     res["cost_fit_us"] = {"per_kstep": float(alpha), "fixed": float(beta)}
-    # the dynamic scheduler handing out the longest-K problems first
-    lplan = ptg.gemm_create(tile_edge=256, log_capacity=1024, group_order=1)
-    ptg.gemm_run_grouped(As, Bs, Cs, lplan, mode="dynamic", stream=stream)
-    ms_ev = time_runs(lambda: ptg.gemm_run_grouped(As, Bs, Cs, lplan, mode="dynamic", stream=stream), 5, 1, stream)
-    ptg.gemm_run_grouped(As, Bs, Cs, lplan, mode="dynamic", stream=stream)
-    ms = makespan_from_log(ptg.gemm_read_log(lplan), khz)
-    ms["kernel_ms"] = ms_ev
-    ms["tflops"] = w.flops / (ms_ev * 1e-3) / 1e12
-    res["dynamic_longest_k_first"] = ms
     lplan.destroy()
     res["dynamic_beats_static"] = bool(res["dynamic"]["makespan_us"] < res["static"]["makespan_us"])
     out["grouped_uneven"] = res
@@ -211,30 +225,35 @@ def run_tail_sections(ptg, torch, stream, khz, square):
         A = ptg.bf16_from_bits(q.a_bits)
         B = ptg.bf16_from_bits(q.b_bits)
         C = torch.empty((q.M, q.N), dtype=torch.float32, device="cuda")
-        r = {}
-        for mode in modes:
-            ms_ev = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream), 5, 2, stream)
-            ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
-            rec = ptg.gemm_read_log(plan)
-            ms = makespan_from_log(rec, khz)
-            ms["kernel_us"] = ms_ev * 1e3
-            ms["hbm_gbs"] = (q.M * q.K * 2 + q.K * q.N * 2 + q.M * q.N * 4) / (ms_ev * 1e-3) / 1e9
-            r[mode] = ms
+        variants = {mode: (mode, plan) for mode in modes}
+        splan = None
         if name == "tail_257":
             # the one tile of the partial last wave split into (at most 4) K-chunks over idle workers
             splan = ptg.gemm_create(tile_edge=256, log_capacity=512, tail_split=4)
-            for mode in ("static", "dynamic"):
-                ms_ev = time_runs(lambda: ptg.gemm_run(A, B, C, splan, mode=mode, stream=stream), 5, 2, stream)
-                ptg.gemm_run(A, B, C, splan, mode=mode, stream=stream)
-                rec = ptg.gemm_read_log(splan)
-                info = ptg.gemm_plan_info_get(splan)
-                ms = makespan_from_log(rec, khz)
-                ms["kernel_us"] = ms_ev * 1e3
+            variants["static_tail_split"] = ("static", splan)
+            variants["dynamic_tail_split"] = ("dynamic", splan)
+        fns = {v: (lambda mode=mode, pl=pl: ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream))
+               for v, (mode, pl) in variants.items()}
+        kernel_ms = time_interleaved(fns, rounds=4, per_round=5, stream=stream)
+
+        def logged(fn, pl):
+            fn()
+            torch.cuda.synchronize()
+            return ptg.gemm_read_log(pl), {}
+        r = {}
+        for v, (mode, pl) in variants.items():
+            ms, _ = median_run(lambda: logged(fns[v], pl), khz)
+            ms["kernel_us"] = kernel_ms[v] * 1e3
+            if pl is plan:
+                ms["hbm_gbs"] = (q.M * q.K * 2 + q.K * q.N * 2 + q.M * q.N * 4) / (kernel_ms[v] * 1e-3) / 1e9
+            else:
+                info = ptg.gemm_plan_info_get(pl)
                 ms["units"] = int(info["last_units"])
                 ms["chunks"] = int(info["last_split_chunks"])
-                whole = r[mode]["tile_median_us"]
-                ms["makespan_t"] = ms["makespan_us"] / whole
-                r[mode + "_tail_split"] = ms
+                ms["makespan_t"] = ms["makespan_us"] / r[mode]["tile_median_us"]
+            r[v] = ms
+        if splan is not None:
+            splan.destroy()
         res[name] = r
         del A, B, C
     out["tail_boundary"] = res
@@ -250,11 +269,15 @@ def run_tail_sections(ptg, torch, stream, khz, square):
     plan = ptg.gemm_create(tile_edge=128, log_capacity=64, max_concurrent=3, static_workers=4, claim_policy=0,
                            min_lds_bytes=96 * 1024)
     res = {}
+
+    def logged_we(mode):
+        ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
+        torch.cuda.synchronize()
+        return ptg.gemm_read_log(plan), {}
     for mode in modes:
-        for _ in range(3):
+        for _ in range(2):
             ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
-        rec = ptg.gemm_read_log(plan)
-        res[mode] = makespan_from_log(rec, khz)
+        res[mode], _ = median_run(lambda: logged_we(mode), khz, n=5)
     # makespan in units of each mode's own median tile time (the pages' t)
     for mode in modes:
         res[mode]["makespan_t"] = res[mode]["makespan_us"] / res[mode]["tile_median_us"]
