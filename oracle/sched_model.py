@@ -114,13 +114,18 @@ def _check_invariants(T: int, tiles: List[Optional[TileRun]], workers: Dict[int,
 def simulate(costs: Sequence[float], mode: str, slots: Optional[int] = None,
              avail: Optional[Sequence[float]] = None, P: Optional[int] = None,
              launch_cost: float = 0.0, claim_cost: float = 0.0, claims_ahead: int = 0,
-             counter_start: int = 0) -> Schedule:
+             counter_start: int = 0, tie_rank: Optional[Sequence[int]] = None) -> Schedule:
     """Run the model. ``costs[k]`` is the duration of tile k (tiles in raster order).
 
     Exactly one of ``slots`` (all usable at time 0) or ``avail`` (per-slot start
     times) gives the execution slots. ``P`` is the static worker count (default:
     the number of slots). ``counter_start`` presets the dynamic claim counter
     (tiles below it are treated as already taken and are not run).
+    ``tie_rank`` (a permutation of the workgroup indices) replaces the workgroup
+    index as the tie-break between workgroup events at one instant with equal
+    claim counts (assumption 3): any order in which simultaneous claims reach the
+    counter can be modelled, the GPU's atomics resolving them in an order the
+    model does not know.
     """
     if mode not in MODES:
         raise ValueError(f"mode must be one of {MODES}")
@@ -140,6 +145,9 @@ def simulate(costs: Sequence[float], mode: str, slots: Optional[int] = None,
         G = T
     if mode == "dynamic" and not (0 <= counter_start):
         raise ValueError("counter_start must be >= 0")
+    rank = list(range(G)) if tie_rank is None else [int(r) for r in tie_rank]
+    if sorted(rank) != list(range(G)):
+        raise ValueError("tie_rank must be a permutation of the workgroup indices")
 
     tiles: List[Optional[TileRun]] = [None] * T
     workers: Dict[int, WorkerRun] = {}
@@ -166,7 +174,7 @@ def simulate(costs: Sequence[float], mode: str, slots: Optional[int] = None,
     failed: Dict[int, bool] = {}
 
     def wkey(w: int):
-        return (workers[w].claims, w)
+        return (workers[w].claims, rank[w])
 
     def finish(w: int, now: float) -> None:
         workers[w].exit = now
@@ -194,7 +202,7 @@ def simulate(costs: Sequence[float], mode: str, slots: Optional[int] = None,
                 w = next_wg[0]
                 next_wg[0] += 1
                 workers[w] = WorkerRun(w, s, now, now, [])
-                push(now + launch_cost, 1, (0, w), "enter", w)
+                push(now + launch_cost, 1, (0, rank[w]), "enter", w)
             continue
         w = payload
         if kind == "enter":

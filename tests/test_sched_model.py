@@ -210,3 +210,24 @@ def test_lpt_order_meets_grahams_bound_and_helps_uneven_costs():
     assert simulate(c, "dynamic", slots=4).makespan == 10
     order = lpt_claim_order(c, [1] * 9)
     assert simulate([c[t] for t in order], "dynamic", slots=4).makespan == 8
+
+
+@pytest.mark.parametrize("q", [0, 1])
+def test_every_tie_order_keeps_exactly_once_and_the_equal_cost_makespan(q):
+    # Simultaneous claims reach the counter in an order the model cannot know (the GPU's atomics decide
+    # it). Over every order of the workgroups at each instant (all permutations, T <= 6), every tile
+    # still runs exactly once (asserted inside the model), each worker's tiles still increase, and with
+    # equal costs on S free slots the makespan is still ceil(T / S) * t.
+    import itertools
+    for T in range(1, 7):
+        for S in (1, 2, 3):
+            for perm in itertools.permutations(range(T)):
+                sch = simulate([1.0] * T, "dynamic", slots=S, claims_ahead=q, tie_rank=perm)
+                assert sch.makespan == pytest.approx(math.ceil(T / S)), (T, S, perm, sch.makespan)
+                for w in sch.workers.values():
+                    assert w.tiles == sorted(w.tiles)
+
+
+def test_tie_rank_must_be_a_permutation():
+    with pytest.raises(ValueError):
+        simulate([1.0] * 3, "dynamic", slots=2, tie_rank=[0, 0, 1])
