@@ -469,7 +469,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // 16 x 16 main loop places its reads and loads itself.)
     constexpr int kReads = CF::MI + 2 * CF::NI;
     auto read_frags = [&](int st, int s, bf16x8(&af)[CF::MI], bf16x8(&bfr)[CF::NI], int lst, int32_t kt_load,
-                          int count) {
+                          int count, const uint32_t *voff_fast = nullptr) {
       const unsigned char *sa = smem + st * CF::STAGE;
       const unsigned char *sb = sa + CF::A_STAGE;
       i32x4 ra = {0, 0, 0, 0}, rb = {0, 0, 0, 0};
@@ -499,7 +499,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 #pragma unroll
         for (int j = 0; j < count; ++j)
           if (j == r)
-            load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j), load_voff(j, kt_load));
+            load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j),
+                          voff_fast ? voff_fast[j] : load_voff(j, kt_load));
       }
     };
 
@@ -548,10 +549,16 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         wg_barrier();
         bf16x8 a0[CF::MI], b0[CF::NI], a1[CF::MI], b1[CF::NI];
         read_frags(0, 0, a0, b0, 0, 0, 0);
-        for (int32_t kt = kb; kt < ke; ++kt) {
+        // load offsets of a k-step with no partial K, once per tile (as in the
+        // 16 x 16 loop); steps whose loads reach the partial k-step `full` use
+        // the K-tail test
+        uint32_t voff_fast[kLoads];
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) voff_fast[j] = load_voff_edge(j);
+        const int32_t slow_from = (K % CF::BK != 0 && full < ke) ? max(kb, full - 3) : ke;
+        auto step = [&](int32_t kt, bool fast) {
           const int st = (kt - kb) & 3;
-          if (kt == claim_at) do_claims();
-          read_frags(st, 1, a1, b1, (st + 3) & 3, kt + 3, kLoads);
+          read_frags(st, 1, a1, b1, (st + 3) & 3, kt + 3, kLoads, fast ? voff_fast : nullptr);
           mma(a0, b0);
           interleave<kReads, kMfma>();
           // stage st fully read and stage st+1 landed (its loads went out two k-steps
@@ -562,7 +569,18 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
           read_frags((st + 1) & 3, 0, a0, b0, 0, 0, 0);
           mma(a1, b1);
           interleave<kReads, kMfma>();
+        };
+        int32_t kt = kb;
+        auto steps = [&](int32_t end) {
+          for (const int32_t fe = min(end, slow_from); kt < fe; ++kt) step(kt, true);
+          for (; kt < end; ++kt) step(kt, false);
+        };
+        // the claims go out between two runs of the loop (no branch for them in a step)
+        if constexpr (MODE == kDynamic) {
+          steps(claim_at >= kb ? claim_at : ke);
+          if (claim_at >= kb) do_claims();
         }
+        steps(ke);
       }
     } else {
       if (ke > kb) {
