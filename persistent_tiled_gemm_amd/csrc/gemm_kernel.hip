@@ -72,6 +72,13 @@ struct Cfg {
   static constexpr int B_ROW_CHUNKS = BN / 8;
   static constexpr int STAGE = A_STAGE + B_STAGE;
   static constexpr int LDS = NSTAGE * STAGE;
+  // LDS placement: the four B stages first, then the four A stages, so that
+  // every fragment read of a stage known at compile time is a per-lane base
+  // plus an offset that fits the 16-bit offset field of ds_read (the A base
+  // carries the B region's size)
+  static constexpr int B_REGION = NSTAGE * B_STAGE;
+  static constexpr int a_off(int s) { return B_REGION + s * A_STAGE; }
+  static constexpr int b_off(int s) { return s * B_STAGE; }
   static_assert(A_LOADS * THREADS == BM * (BK / 8) && B_LOADS * THREADS == BK * (BN / 8), "load split");
   static_assert(WM % MB == 0 && WN % MB == 0 && (MB == 16 || MB == 32), "wave tile");
 };
@@ -420,19 +427,19 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
                                              : k0 + (int32_t)(b_k0 + kBRowsPerJ * (uint32_t)(j - CF::A_LOADS));
       return kfirst >= K ? kBufOob : vo;
     };
-    auto load_dst = [&](int j) -> uint32_t {
-      return j < CF::A_LOADS ? (uint32_t)(j * CF::NW + (int)wave) * 1024u
-                             : (uint32_t)CF::A_STAGE + (uint32_t)((j - CF::A_LOADS) * CF::NW + (int)wave) * 1024u;
+    // LDS byte offset (from smem) of load j's 1 KiB block in stage st
+    auto load_dst = [&](int j, int st) -> uint32_t {
+      return j < CF::A_LOADS ? (uint32_t)CF::a_off(st) + (uint32_t)(j * CF::NW + (int)wave) * 1024u
+                             : (uint32_t)CF::b_off(st) + (uint32_t)((j - CF::A_LOADS) * CF::NW + (int)wave) * 1024u;
     };
     // all loads of k-step kt into stage dst, back to back (prologue)
     auto issue_all = [&](int st, int32_t kt) {
-      unsigned char *dst = smem + st * CF::STAGE;
       const i32x4 ra = make_rsrc_words(a_tile + kt * CF::BK, kt < ke);
       const i32x4 rb = make_rsrc_words(b_tile + (size_t)(kt * CF::BK) * (size_t)N, kt < ke);
-      const uint32_t base = lds_addr(dst);
+      const uint32_t base = lds_addr(smem);
 #pragma unroll
       for (int j = 0; j < CF::A_LOADS + CF::B_LOADS; ++j)
-        load16_to_lds(j < CF::A_LOADS ? ra : rb, base + load_dst(j), load_voff(j, kt));
+        load16_to_lds(j < CF::A_LOADS ? ra : rb, base + load_dst(j, st), load_voff(j, kt));
     };
 
     // fragment read offsets (bytes inside a stage). An MFMA operand is 8
@@ -470,14 +477,13 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     constexpr int kReads = CF::MI + 2 * CF::NI;
     auto read_frags = [&](int st, int s, bf16x8(&af)[CF::MI], bf16x8(&bfr)[CF::NI], int lst, int32_t kt_load,
                           int count, const uint32_t *voff_fast = nullptr) {
-      const unsigned char *sa = smem + st * CF::STAGE;
-      const unsigned char *sb = sa + CF::A_STAGE;
+      const unsigned char *sa = smem + CF::a_off(st);
+      const unsigned char *sb = smem + CF::b_off(st);
       i32x4 ra = {0, 0, 0, 0}, rb = {0, 0, 0, 0};
-      uint32_t lbase = 0;
+      const uint32_t lbase = lds_addr(smem);
       if (count > 0) {
         ra = make_rsrc_words(a_tile + kt_load * CF::BK, kt_load < ke);
         rb = make_rsrc_words(b_tile + (size_t)(kt_load * CF::BK) * (size_t)N, kt_load < ke);
-        lbase = lds_addr(smem + lst * CF::STAGE);
       }
       i16x4 lo[CF::NI];
 #pragma unroll
@@ -499,7 +505,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 #pragma unroll
         for (int j = 0; j < count; ++j)
           if (j == r)
-            load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j),
+            load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j, lst),
                           voff_fast ? voff_fast[j] : load_voff(j, kt_load));
       }
     };
@@ -625,16 +631,18 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         // FAST: the k-step's loads read whole 32-deep slices (or lie past the
         // unit and read zeros through the resource), so the offsets above serve;
         // otherwise they are computed with the K-tail test.
-        auto step = [&](auto fast, int32_t kt, const bf16x8(&ac)[CF::MI], const bf16x8(&bc)[CF::NI],
+        // st: the stage step kt's fragments came from, (kt - kb) mod 4; a compile-time
+        // constant in the four-step trips, so every LDS address of the step is a
+        // per-lane base plus an immediate offset
+        auto step = [&](auto fast, int32_t kt, int st, const bf16x8(&ac)[CF::MI], const bf16x8(&bc)[CF::NI],
                         bf16x8(&an)[CF::MI], bf16x8(&bn)[CF::NI]) {
-          const int st = (kt - kb) & 3;
           const int rst = (st + 1) & 3;
-          const unsigned char *sa = smem + rst * CF::STAGE;
-          const unsigned char *sb = sa + CF::A_STAGE;
+          const unsigned char *sa = smem + CF::a_off(rst);
+          const unsigned char *sb = smem + CF::b_off(rst);
           const int32_t kt_load = kt + 4;
           const i32x4 ra = make_rsrc_words(a_tile + kt_load * CF::BK, kt_load < ke);
           const i32x4 rb = make_rsrc_words(b_tile + (size_t)(kt_load * CF::BK) * (size_t)N, kt_load < ke);
-          const uint32_t lbase = lds_addr(smem + st * CF::STAGE);
+          const uint32_t lbase = lds_addr(smem);
           i16x4 lo[CF::NI];
 #pragma unroll
           for (int i = 0; i < kMfma; ++i) {
@@ -658,7 +666,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 #pragma unroll
               for (int j = 0; j < kLoads; ++j)
                 if (j * kReads / kLoads == r)
-                  load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j),
+                  load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j, st),
                                 decltype(fast)::value ? voff_fast[j] : load_voff(j, kt_load));
             }
           }
@@ -684,20 +692,32 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         // offsets.
         const int32_t slow_from =
             (K % CF::BK != 0 && full < ke) ? kb + ((max(full - 5 - kb, 0) + 1) / 2) * 2 : ke + 2;
+        // Fast trips of four steps while whole ones fit (constant stages), then
+        // two-step trips with the stage computed at run time. A run starts with
+        // kt - kb a multiple of 4.
         auto trips = [&](int32_t &kt, int32_t end) {
           const int32_t fast_end = min(end, slow_from);
+          for (; kt + 4 <= fast_end; kt += 4) {
+            step(std::true_type{}, kt, 0, a0, b0, a1, b1);
+            step(std::true_type{}, kt + 1, 1, a1, b1, a0, b0);
+            step(std::true_type{}, kt + 2, 2, a0, b0, a1, b1);
+            step(std::true_type{}, kt + 3, 3, a1, b1, a0, b0);
+          }
           for (; kt < fast_end; kt += 2) {
-            step(std::true_type{}, kt, a0, b0, a1, b1);
-            step(std::true_type{}, kt + 1, a1, b1, a0, b0);
+            const int st = (kt - kb) & 3;
+            step(std::true_type{}, kt, st, a0, b0, a1, b1);
+            step(std::true_type{}, kt + 1, (st + 1) & 3, a1, b1, a0, b0);
           }
           for (; kt < end; kt += 2) {
-            step(std::false_type{}, kt, a0, b0, a1, b1);
-            step(std::false_type{}, kt + 1, a1, b1, a0, b0);
+            const int st = (kt - kb) & 3;
+            step(std::false_type{}, kt, st, a0, b0, a1, b1);
+            step(std::false_type{}, kt + 1, (st + 1) & 3, a1, b1, a0, b0);
           }
         };
         int32_t kt = kb;
         if constexpr (MODE == kDynamic) {
-          const int32_t split_at = claim_at >= kb ? kb + ((claim_at - kb) & ~1) : ke;
+          // the claims go out at the four-step boundary at or before claim_at
+          const int32_t split_at = claim_at >= kb ? kb + ((claim_at - kb) & ~3) : ke;
           trips(kt, split_at);
           claim_issue_asm(claim_ctr, batch_n >= 1u, batch[0]);
           claim_issue_asm(claim_ctr, batch_n >= 2u, batch[1]);

@@ -76,22 +76,34 @@ def slots(line):
 CASES = [(m, g) for m in (0, 1, 2) for g in (False, True)]
 
 
+def loop_blocks(text, split_asm_labels=False):
+    pattern = r"\n(?:\.LBB\d+_\d+|\d+):" if split_asm_labels else r"\n\.LBB\d+_\d+:"
+    blocks = re.split(pattern, text)
+    return [instructions(b) for b in blocks if sum(1 for x in instructions(b) if x.startswith("v_mfma_f32_16x16")) > 0]
+
+
+# each run of the loop has three forms: four-step trips with load offsets computed once per tile
+# and compile-time stages, two-step trips with the same offsets, and two-step K-tail trips; the
+# dynamic scheduler runs the loop in two parts and claims in between
+def expected_loops(mode):
+    return 6 if mode == 2 else 3
+
+
 @pytest.mark.parametrize("mode,grouped", CASES)
 def test_main_loop_is_one_block_without_copies(asm, mode, grouped):
-    text = kernel_lines(asm, mode, grouped)
-    blocks = re.split(r"\n\.LBB\d+_\d+:", text)
-    loops = [instructions(b) for b in blocks if sum(1 for x in instructions(b) if x.startswith("v_mfma_f32_16x16")) > 0]
-    # each run of the loop has a fast form (load offsets computed once per tile) and a K-tail form;
-    # the dynamic scheduler runs the loop in two parts and claims in between
-    assert len(loops) == (4 if mode == 2 else 2), "the 16 x 16 MFMAs of a trip sit in more than one basic block"
+    loops = loop_blocks(kernel_lines(asm, mode, grouped))
+    assert len(loops) == expected_loops(mode), "the 16 x 16 MFMAs of a trip sit in more than one basic block"
     for body in loops:
-        assert sum(1 for x in body if x.startswith("v_mfma_f32_16x16x32_bf16")) == 128
+        mfma = sum(1 for x in body if x.startswith("v_mfma_f32_16x16x32_bf16"))
+        assert mfma in (128, 256), mfma  # 64 per k-step, two or four k-steps per trip
+        steps = mfma // 64
         assert not [x for x in body if x.startswith(("v_accvgpr_read", "v_accvgpr_write", "v_accvgpr_mov"))]
         assert not [x for x in body if x.startswith("scratch_")]
         assert not [x for x in body if x.startswith("s_waitcnt") and "vmcnt(0)" in x]
         # four LDS stages: the end-of-step waits leave two steps of loads in flight
-        assert sum(1 for x in body if x.startswith("s_waitcnt") and "vmcnt(16)" in x) == 2
-        assert sum(1 for x in body if x.startswith("s_barrier")) == 2
+        assert sum(1 for x in body if x.startswith("s_waitcnt") and "vmcnt(16)" in x) == steps
+        assert sum(1 for x in body if x.startswith("s_barrier")) == steps
+    assert sum(1 for body in loops if sum(1 for x in body if x.startswith("v_mfma")) == 256) == expected_loops(mode) // 3
 
 
 @pytest.mark.parametrize("mode,grouped", CASES)
@@ -99,17 +111,14 @@ def test_main_loop_has_no_claim_branch_or_exec_write(asm, mode, grouped):
     """A branch or an EXEC write inside a k-step holds the wave until the MFMAs in
     flight drain (measured 70-90 cycles per step), so a trip's only branch is its
     back edge and nothing in it writes EXEC or sends an atomic."""
-    text = kernel_lines(asm, mode, grouped)
-    # split at every label, the assembly statements' local labels included
-    blocks = re.split(r"\n(?:\.LBB\d+_\d+|\d+):", text)
-    loops = [instructions(b) for b in blocks if sum(1 for x in instructions(b) if x.startswith("v_mfma_f32_16x16")) > 0]
-    assert len(loops) == (4 if mode == 2 else 2)
+    loops = loop_blocks(kernel_lines(asm, mode, grouped), split_asm_labels=True)
+    assert len(loops) == expected_loops(mode)
     for body in loops:
         # the trip ends at its back edge (the block's text may run on past it)
         ends = [n for n, x in enumerate(body) if x.startswith(("s_cbranch", "s_branch", "s_setpc"))]
         assert ends, "no back edge"
         body = body[: ends[0] + 1]
-        assert sum(1 for x in body if x.startswith("v_mfma_f32_16x16x32_bf16")) == 128
+        assert sum(1 for x in body if x.startswith("v_mfma_f32_16x16x32_bf16")) in (128, 256)
         assert not [x for x in body if "exec" in x.split(",")[0] or x.startswith("s_and_saveexec")]
         assert not [x for x in body if x.startswith(("global_atomic", "buffer_atomic", "flat_atomic"))]
 
@@ -165,16 +174,17 @@ def test_mfma_hazard_distances(asm, mode, grouped):
 @pytest.mark.parametrize("mode,grouped", CASES)
 def test_fast_trips_compute_no_load_masks(asm, mode, grouped):
     """Vector instructions interleaved with the MFMAs stall them (recomputing the load masks every
-    k-step cost about 220 cycles per step), so half of the trips, those with no partial K, carry
-    only the LDS read address adds: at most 24 non-MFMA vector instructions per trip of two
-    k-steps (the K-tail trips carry about 65)."""
-    text = kernel_lines(asm, mode, grouped)
-    blocks = re.split(r"\n\.LBB\d+_\d+:", text)
-    loops = [instructions(b) for b in blocks if sum(1 for x in instructions(b) if x.startswith("v_mfma_f32_16x16")) > 0]
+    k-step cost about 220 cycles per step; the LDS read address adds about 80 more), so the
+    four-step trips, whose stages are compile-time constants, hold no vector instruction besides
+    the MFMAs, and the two-step trips with precomputed load offsets at most 24 (the K-tail trips
+    carry about 56)."""
     valu = []
-    for body in loops:
+    for body in loop_blocks(kernel_lines(asm, mode, grouped)):
         ends = [n for n, x in enumerate(body) if x.startswith(("s_cbranch", "s_branch"))]
         body = body[: ends[0] + 1]
-        valu.append(sum(1 for x in body if x.startswith("v_") and not x.startswith("v_mfma")))
-    fast = [v for v in valu if v <= 24]
-    assert len(fast) == len(loops) // 2, valu
+        mfma = sum(1 for x in body if x.startswith("v_mfma"))
+        valu.append((mfma, sum(1 for x in body if x.startswith("v_") and not x.startswith("v_mfma"))))
+    runs = expected_loops(mode) // 3
+    assert sorted(v for m, v in valu if m == 256) == [0] * runs, valu
+    two = sorted(v for m, v in valu if m == 128)
+    assert len(two) == 2 * runs and all(v <= 24 for v in two[:runs]) and all(v > 24 for v in two[runs:]), valu
