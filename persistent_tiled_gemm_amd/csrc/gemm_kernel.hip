@@ -9,8 +9,9 @@
 // round trip) into a ring of four 32-deep LDS stages, each load two to three
 // k-steps ahead of its first reader.
 //
-// LDS layouts (16-byte chunks, XOR-swizzled so fragment reads are bank-conflict
-// free):
+// LDS layouts: the four B stages first, then the four A stages (so that reads
+// of a stage known at compile time need no address arithmetic in the loop);
+// 16-byte chunks, XOR-swizzled so fragment reads are bank-conflict free:
 //   A stage: BM rows x 32 k, 64 B per row; logical chunk c of row r sits in slot
 //            c ^ ((r >> 1) & 3) (16 x 16 blocks) or c ^ ((r >> 2) & 3) (32 x 32).
 //            A fragments are read with ds_read_b128 (8 consecutive k of one row
