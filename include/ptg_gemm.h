@@ -100,13 +100,13 @@ typedef enum gemm_sched_mode {
  *   claim_lead      with claims_ahead >= 1, the claims for later tiles are issued
  *                   at the start of k-step c = max(0, nk - claim_lead) of the
  *                   current tile (nk = its number of 32-deep k-steps); with
- *                   256 x 256 tiles at the start of the pair of k-steps that
- *                   holds c, i.e. k-step c or c - 1 (the main loop runs two
- *                   k-steps per trip and claims only between trips). Late, so a
- *                   worker does not take work a not-yet-started slot would get,
- *                   yet early enough for the atomic's round trip to hide under
- *                   the MFMAs. 0 = at the last k-step (or pair); >= nk = at the
- *                   tile start.
+ *                   256 x 256 tiles at the start of the group of four k-steps
+ *                   (counted from the tile's first) that holds c, i.e. one of
+ *                   k-steps c - 3 .. c (the main loop runs four k-steps per trip
+ *                   and claims only between trips). Late, so a worker does not
+ *                   take work a not-yet-started slot would get, yet early enough
+ *                   for the atomic's round trip to hide under the MFMAs. 0 = at
+ *                   the last k-step (or group); >= nk = at the tile start.
  *   claim_policy    0 = one device-wide counter hands out tile ids in order.
  *                   1 = XCD-partitioned: tile ids with id mod 8 == x form region
  *                   x, handed out by counter x; a worker claims from the region
