@@ -382,6 +382,10 @@ def main():
                 ("dynamic_claim_groups_2x2", "dynamic", plan_group)]
         fns = {name: (lambda mode=mode, pl=pl: ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream))
                for name, mode, pl in runs}
+        # the same product with B given as N x K (plan b_layout 1: C = A . Bt^T)
+        plan_bt = ptg.gemm_create(**dict(fields, b_layout=1))
+        Bt = B.t().contiguous()
+        fns["dynamic_b_transposed"] = lambda: ptg.gemm_run(A, Bt, C, plan_bt, mode="dynamic", stream=stream)
         # context only: the vendor library's bf16 GEMM at the same shape (torch.matmul -> hipBLASLt), which
         # writes a bf16 C (half of our fp32 C bytes), and, where torch offers it, the same product with an
         # fp32 C (torch.mm with out_dtype), the exact counterpart of this kernel
@@ -405,6 +409,8 @@ def main():
                 modes[name].update(makespan_us=mk["makespan_us"], tile_median_us=mk["tile_median_us"])
         plan_other.destroy()
         plan_group.destroy()
+        plan_bt.destroy()
+        del Bt
 
     roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(1.0),

@@ -145,6 +145,11 @@ typedef enum gemm_sched_mode {
  *                   2 x h block of tiles sharing A and B panels, the claim-sized
  *                   counterpart of a cluster. Exclusive with tail_split (a
  *                   claim group wins).
+ *   b_layout        0 = B is K x N row-major (C = A . B, torch.matmul(A, B)).
+ *                   1 = B is given as N x K row-major, i.e. the product is
+ *                   C = A . B^T (torch.matmul(A, Bt.T)); its rows are K long,
+ *                   so the same K % 8 and N % 8 rules apply. Applies to the
+ *                   plan's single and grouped runs alike.
  */
 typedef struct gemm_tile_desc {
   int32_t bm, bn, bk;
@@ -163,6 +168,7 @@ typedef struct gemm_tile_desc {
   int32_t tail_split;
   int32_t group_order;
   int32_t claim_group;
+  int32_t b_layout;
 } gemm_tile_desc;
 
 /* Opaque plan: the tile_cfg argument of gemm_run. Owns all library scratch. */

@@ -51,7 +51,8 @@ class PtgError(RuntimeError):
 class TileDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bm", "bn", "bk", "ring_depth", "claims_ahead", "claim_lead", "claim_policy", "raster", "raster_group", "static_workers",
-        "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device", "tail_split", "group_order", "claim_group")]
+        "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device", "tail_split", "group_order", "claim_group",
+        "b_layout")]
 
 
 class TileRec(ctypes.Structure):
@@ -199,7 +200,7 @@ def _stream_ptr(stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _check_operands(A, B, C):
+def _check_operands(A, B, C, b_layout: int = 0):
     import torch
     for name, t, dts in (("A", A, (torch.bfloat16, torch.int16, torch.uint16)),
                          ("B", B, (torch.bfloat16, torch.int16, torch.uint16)), ("C", C, (torch.float32,))):
@@ -212,7 +213,7 @@ def _check_operands(A, B, C):
         if t.dim() != 2:
             raise ValueError(f"{name} must be 2-D")
     M, K = A.shape
-    K2, N = B.shape
+    K2, N = B.shape if b_layout == 0 else tuple(B.shape)[::-1]  # b_layout 1: B is N x K
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
     return int(M), int(N), int(K)
@@ -227,8 +228,9 @@ def _mode(mode) -> int:
 
 
 def gemm_run(A, B, C, plan: Plan, mode="dynamic", stream=None) -> None:
-    """gemm_run: enqueue C = A.B (A: M x K bf16, B: K x N bf16, C: M x N fp32)."""
-    M, N, K = _check_operands(A, B, C)
+    """gemm_run: enqueue C = A.B (A: M x K bf16, B: K x N bf16, C: M x N fp32); with a plan of
+    b_layout 1, B is N x K and C = A.B^T."""
+    M, N, K = _check_operands(A, B, C, int(plan.desc.b_layout))
     st = load_library().gemm_run(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
                                  ctypes.c_void_p(C.data_ptr()), M, N, K, _mode(mode), plan.handle,
                                  ctypes.c_void_p(_stream_ptr(stream)))
@@ -249,7 +251,7 @@ def gemm_run_grouped(As: Sequence, Bs: Sequence, Cs: Sequence, plan: Plan, mode=
     G = len(As)
     if not (len(Bs) == len(Cs) == G) or G == 0:
         raise ValueError("need equally many A, B, C (at least one)")
-    dims = [_check_operands(a, b, c) for a, b, c in zip(As, Bs, Cs)]
+    dims = [_check_operands(a, b, c, int(plan.desc.b_layout)) for a, b, c in zip(As, Bs, Cs)]
     VP = ctypes.c_void_p * G
     I64 = ctypes.c_int64 * G
     st = load_library().gemm_run_grouped(
@@ -328,7 +330,8 @@ def matmul(A, B, mode="dynamic", plan: Optional[Plan] = None, stream=None):
     own = plan is None
     if own:
         plan = gemm_create()
-    C = torch.empty((A.shape[0], B.shape[1]), dtype=torch.float32, device=A.device)
+    n = B.shape[1] if int(plan.desc.b_layout) == 0 else B.shape[0]
+    C = torch.empty((A.shape[0], n), dtype=torch.float32, device=A.device)
     try:
         gemm_run(A, B, C, plan, mode=mode, stream=stream)
         if own:

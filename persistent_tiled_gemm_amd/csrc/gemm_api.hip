@@ -170,7 +170,7 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   args.clear_next = reinterpret_cast<uint32_t *>(nxt + kArrivalsOffset);
   args.clear_count = ptg::kMaxSplitTiles + p->desc.log_capacity;
   args.log = p->d_log;
-  hipError_t e = ptg::launch_gemm(p->desc.bm, mode, grouped, args, (int)grid, p->dyn_lds, s);
+  hipError_t e = ptg::launch_gemm(p->desc.bm, mode, grouped, p->desc.b_layout == 1, args, (int)grid, p->dyn_lds, s);
   if (e != hipSuccess) return hip_fail(p, e, "kernel launch");
   ++p->runs;
   p->last_stream = s;
@@ -226,6 +226,7 @@ gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t de
   out->tail_split = 0;
   out->group_order = 0;
   out->claim_group = 1;
+  out->b_layout = 0;
   return GEMM_OK;
 }
 
@@ -240,7 +241,8 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (d.raster < 0 || d.raster > 1 || (d.raster == 1 && d.raster_group < 1)) return GEMM_E_INVALID_ARG;
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
       d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT || d.group_order < 0 ||
-      d.group_order > 1 || d.claim_group < 0 || d.claim_group > GEMM_MAX_CLAIM_GROUP)
+      d.group_order > 1 || d.claim_group < 0 || d.claim_group > GEMM_MAX_CLAIM_GROUP || d.b_layout < 0 ||
+      d.b_layout > 1)
     return GEMM_E_INVALID_ARG;
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);

@@ -220,7 +220,9 @@ __device__ __forceinline__ uint32_t claim_next(const KernelArgs &a, uint32_t xcc
   return claim_resolve(a, xcc, lane, raw, region);
 }
 
-template <int BM, int BN, int MODE, bool GROUPED>
+// BT: B is given as N x K row-major (C = A . B^T); its stage then holds BN rows
+// x 32 k like A's, and its fragments are read like A's.
+template <int BM, int BN, int MODE, bool GROUPED, bool BT>
 __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel(const KernelArgs args) {
   using CF = typename TileCfg<BM>::type;
   static_assert(CF::BM_ == BM && CF::BN_ == BN, "config");
@@ -388,8 +390,14 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     const uint32_t b_base0 = n0 + (int32_t)(b_c0 * 8u) < N ? (b_k0 * (uint32_t)N + b_c0 * 8u) * 2u : kBufOob;
     const uint32_t b_base1 = n0 + (int32_t)(b_c1 * 8u) < N ? (b_k0 * (uint32_t)N + b_c1 * 8u) * 2u : kBufOob;
     const int32_t m_left = M - m0;  // rows of A that exist in this tile
+    const int32_t n_left = N - n0;  // rows of B^T that exist in this tile (BT)
     const uint16_t *a_tile = pb.A + (size_t)m0 * (size_t)K;
-    const uint16_t *b_tile = pb.B + n0;
+    // the k-step enters through the resource base: + kt BK elements along a row
+    // of A (and of B^T), + kt BK rows of B
+    const uint16_t *b_tile = BT ? pb.B + (size_t)n0 * (size_t)K : pb.B + n0;
+    auto b_kstep = [&](int32_t kt) -> const uint16_t * {
+      return BT ? b_tile + kt * CF::BK : b_tile + (size_t)(kt * CF::BK) * (size_t)N;
+    };
     const int32_t nk = (K + CF::BK - 1) / CF::BK;
     const int32_t full = K / CF::BK;  // k-steps with no K tail
     // k-steps [kb, ke) of this unit: all of them, or an even share for a K-chunk
@@ -409,6 +417,13 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         return (int32_t)row >= m_left ? kBufOob : vo;
       }
       const int jb = j - CF::A_LOADS;
+      if constexpr (BT) {
+        // B^T rows like A rows (same row step per load, same swizzle)
+        const uint32_t row = a_row0 + (uint32_t)(CF::A_RPL * CF::NW) * (uint32_t)jb;
+        const uint32_t vo = a_row0 * (uint32_t)K * 2u + load_chunk_a(jb) * 16u +
+                            (uint32_t)(CF::A_RPL * CF::NW * jb) * (uint32_t)K * 2u;
+        return (int32_t)row >= n_left ? kBufOob : vo;
+      }
       const uint32_t bb = ((kBRowsPerJ * (uint32_t)jb) & 8u) ? b_base1 : b_base0;
       return bb == kBufOob ? kBufOob : bb + (uint32_t)jb * kBRowsPerJ * (uint32_t)N * 2u;
     };
@@ -425,7 +440,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       if (kt < full) return vo;
       const int32_t k0 = kt * CF::BK;
       const int32_t kfirst = j < CF::A_LOADS ? k0 + (int32_t)(load_chunk_a(j) * 8u)
-                                             : k0 + (int32_t)(b_k0 + kBRowsPerJ * (uint32_t)(j - CF::A_LOADS));
+                             : BT ? k0 + (int32_t)(load_chunk_a(j - CF::A_LOADS) * 8u)
+                                  : k0 + (int32_t)(b_k0 + kBRowsPerJ * (uint32_t)(j - CF::A_LOADS));
       return kfirst >= K ? kBufOob : vo;
     };
     // LDS byte offset (from smem) of load j's 1 KiB block in stage st
@@ -436,7 +452,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // all loads of k-step kt into stage dst, back to back (prologue)
     auto issue_all = [&](int st, int32_t kt) {
       const i32x4 ra = make_rsrc_words(a_tile + kt * CF::BK, kt < ke);
-      const i32x4 rb = make_rsrc_words(b_tile + (size_t)(kt * CF::BK) * (size_t)N, kt < ke);
+      const i32x4 rb = make_rsrc_words(b_kstep(kt), kt < ke);
       const uint32_t base = lds_addr(smem);
 #pragma unroll
       for (int j = 0; j < CF::A_LOADS + CF::B_LOADS; ++j)
@@ -455,7 +471,16 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       swa[mi] = swz_a<CF::MB>(row) ^ (lane / CF::MB);
     }
     uint32_t off_b[CF::NI];
-    {
+    uint32_t swb[CF::NI];  // BT: the chunk XOR of each block's row, as swa
+    if constexpr (BT) {
+      // a B^T fragment is read like an A fragment: 8 consecutive k of one row n
+#pragma unroll
+      for (int ni = 0; ni < CF::NI; ++ni) {
+        const uint32_t row = wn * CF::WN + ni * CF::MB + (lane % CF::MB);
+        off_b[ni] = row * (uint32_t)CF::A_ROW;
+        swb[ni] = swz_a<CF::MB>(row) ^ (lane / CF::MB);
+      }
+    } else {
       // 32 x 32 blocks: lane group q = lane / 16 covers k half q / 2 and column
       // half q % 2; 16 x 16 blocks: k quarter q of all 16 columns
       const uint32_t q = lane >> 4, i = lane & 15u;
@@ -475,7 +500,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // order between the reads, load j after read j; the reads alternate with
     // MFMAs, so the loads land between MFMAs instead of in one burst. (The
     // 16 x 16 main loop places its reads and loads itself.)
-    constexpr int kReads = CF::MI + 2 * CF::NI;
+    constexpr int kReads = CF::MI + (BT ? 1 : 2) * CF::NI;
     auto read_frags = [&](int st, int s, bf16x8(&af)[CF::MI], bf16x8(&bfr)[CF::NI], int lst, int32_t kt_load,
                           int count, const uint32_t *voff_fast = nullptr) {
       const unsigned char *sa = smem + CF::a_off(st);
@@ -484,13 +509,16 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       const uint32_t lbase = lds_addr(smem);
       if (count > 0) {
         ra = make_rsrc_words(a_tile + kt_load * CF::BK, kt_load < ke);
-        rb = make_rsrc_words(b_tile + (size_t)(kt_load * CF::BK) * (size_t)N, kt_load < ke);
+        rb = make_rsrc_words(b_kstep(kt_load), kt_load < ke);
       }
       i16x4 lo[CF::NI];
 #pragma unroll
       for (int r = 0; r < kReads; ++r) {
         if (r < CF::MI) {
           af[r] = *(const bf16x8 *)(sa + off_a[r] + ((((uint32_t)((CF::KS / 8) * s)) ^ swa[r]) << 4));
+        } else if constexpr (BT) {
+          const int ni = r - CF::MI;
+          bfr[ni] = *(const bf16x8 *)(sb + off_b[ni] + ((((uint32_t)((CF::KS / 8) * s)) ^ swb[ni]) << 4));
         } else {
           const int ni = (r - CF::MI) >> 1;
           const unsigned char *pb0 = sb + off_b[ni] + (CF::KS * s) * CF::B_ROW;
@@ -642,7 +670,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
           const unsigned char *sb = smem + CF::b_off(rst);
           const int32_t kt_load = kt + 4;
           const i32x4 ra = make_rsrc_words(a_tile + kt_load * CF::BK, kt_load < ke);
-          const i32x4 rb = make_rsrc_words(b_tile + (size_t)(kt_load * CF::BK) * (size_t)N, kt_load < ke);
+          const i32x4 rb = make_rsrc_words(b_kstep(kt_load), kt_load < ke);
           const uint32_t lbase = lds_addr(smem);
           i16x4 lo[CF::NI];
 #pragma unroll
@@ -652,6 +680,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
               const int r = i;
               if (r < CF::MI) {
                 an[r] = *(const bf16x8 *)(sa + off_a[r] + (swa[r] << 4));
+              } else if constexpr (BT) {
+                bn[r - CF::MI] = *(const bf16x8 *)(sb + off_b[r - CF::MI] + (swb[r - CF::MI] << 4));
               } else {
                 const int ni = (r - CF::MI) >> 1;
                 const unsigned char *pb0 = sb + off_b[ni];
@@ -910,46 +940,50 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
   }
 }
 
-template <int BM, int BN, int MODE, bool GROUPED>
+template <int BM, int BN, int MODE, bool GROUPED, bool BT>
 static hipError_t launch_one(const KernelArgs &args, int grid, int dyn_lds, hipStream_t stream) {
-  hipLaunchKernelGGL((ptg_gemm_kernel<BM, BN, MODE, GROUPED>), dim3(grid), dim3(TileCfg<BM>::type::THREADS), dyn_lds,
-                     stream, args);
+  hipLaunchKernelGGL((ptg_gemm_kernel<BM, BN, MODE, GROUPED, BT>), dim3(grid), dim3(TileCfg<BM>::type::THREADS),
+                     dyn_lds, stream, args);
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool BT>
 static hipError_t launch_tile(int mode, bool grouped, const KernelArgs &args, int grid, int dyn_lds,
                               hipStream_t stream) {
   switch (mode) {
     case kNonPersistent:
-      return grouped ? launch_one<BM, BN, kNonPersistent, true>(args, grid, dyn_lds, stream)
-                     : launch_one<BM, BN, kNonPersistent, false>(args, grid, dyn_lds, stream);
+      return grouped ? launch_one<BM, BN, kNonPersistent, true, BT>(args, grid, dyn_lds, stream)
+                     : launch_one<BM, BN, kNonPersistent, false, BT>(args, grid, dyn_lds, stream);
     case kStatic:
-      return grouped ? launch_one<BM, BN, kStatic, true>(args, grid, dyn_lds, stream)
-                     : launch_one<BM, BN, kStatic, false>(args, grid, dyn_lds, stream);
+      return grouped ? launch_one<BM, BN, kStatic, true, BT>(args, grid, dyn_lds, stream)
+                     : launch_one<BM, BN, kStatic, false, BT>(args, grid, dyn_lds, stream);
     case kDynamic:
-      return grouped ? launch_one<BM, BN, kDynamic, true>(args, grid, dyn_lds, stream)
-                     : launch_one<BM, BN, kDynamic, false>(args, grid, dyn_lds, stream);
+      return grouped ? launch_one<BM, BN, kDynamic, true, BT>(args, grid, dyn_lds, stream)
+                     : launch_one<BM, BN, kDynamic, false, BT>(args, grid, dyn_lds, stream);
     default:
       return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gemm(int tile_edge, int mode, bool grouped, const KernelArgs &args, int grid, int dyn_lds,
-                       hipStream_t stream) {
-  if (tile_edge == 256) return launch_tile<256, 256>(mode, grouped, args, grid, dyn_lds, stream);
-  if (tile_edge == 128) return launch_tile<128, 128>(mode, grouped, args, grid, dyn_lds, stream);
+hipError_t launch_gemm(int tile_edge, int mode, bool grouped, bool b_transposed, const KernelArgs &args, int grid,
+                       int dyn_lds, hipStream_t stream) {
+  if (tile_edge == 256)
+    return b_transposed ? launch_tile<256, 256, true>(mode, grouped, args, grid, dyn_lds, stream)
+                        : launch_tile<256, 256, false>(mode, grouped, args, grid, dyn_lds, stream);
+  if (tile_edge == 128)
+    return b_transposed ? launch_tile<128, 128, true>(mode, grouped, args, grid, dyn_lds, stream)
+                        : launch_tile<128, 128, false>(mode, grouped, args, grid, dyn_lds, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t gemm_occupancy(int tile_edge, int dyn_lds, int *blocks_per_cu) {
   if (tile_edge == 256)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<256, 256, kDynamic, false>),
+        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<256, 256, kDynamic, false, false>),
         TileCfg<256>::type::THREADS, dyn_lds);
   if (tile_edge == 128)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<128, 128, kDynamic, false>),
+        blocks_per_cu, reinterpret_cast<const void *>(&ptg_gemm_kernel<128, 128, kDynamic, false, false>),
         TileCfg<128>::type::THREADS, dyn_lds);
   return hipErrorInvalidValue;
 }

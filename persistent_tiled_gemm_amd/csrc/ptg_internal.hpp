@@ -79,8 +79,9 @@ struct KernelArgs {
 
 enum SchedMode { kNonPersistent = 0, kStatic = 1, kDynamic = 2 };
 
-// Launch one GEMM kernel instance. tile_edge is 128 or 256.
-hipError_t launch_gemm(int tile_edge, int mode, bool grouped, const KernelArgs &args, int grid,
+// Launch one GEMM kernel instance. tile_edge is 128 or 256; b_transposed: B is
+// given as N x K row-major (C = A . B^T) instead of K x N.
+hipError_t launch_gemm(int tile_edge, int mode, bool grouped, bool b_transposed, const KernelArgs &args, int grid,
                        int dyn_lds_bytes, hipStream_t stream);
 // Resident workgroups per CU for an instance with dyn_lds_bytes of extra LDS.
 hipError_t gemm_occupancy(int tile_edge, int dyn_lds_bytes, int *blocks_per_cu);

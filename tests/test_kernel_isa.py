@@ -43,8 +43,9 @@ def asm(tmp_path_factory):
     return out.read_text()
 
 
-def kernel_lines(asm_text, mode, grouped):
-    name = f"_ZN3ptg15ptg_gemm_kernelILi256ELi256ELi{mode}ELb{1 if grouped else 0}EEEvNS_10KernelArgsE"
+def kernel_lines(asm_text, mode, grouped, bt=False):
+    name = (f"_ZN3ptg15ptg_gemm_kernelILi256ELi256ELi{mode}ELb{1 if grouped else 0}ELb{1 if bt else 0}"
+            "EEEvNS_10KernelArgsE")
     i = asm_text.index(name + ":")
     j = asm_text.index(".Lfunc_end", i)
     return asm_text[i:j]
@@ -74,6 +75,9 @@ def slots(line):
 
 
 CASES = [(m, g) for m in (0, 1, 2) for g in (False, True)]
+# the B^T (N x K) form of the kernel, single GEMMs, every mode
+BT_CASES = [(m, False) for m in (0, 1, 2)]
+ALL_CASES = [(m, g, False) for m, g in CASES] + [(m, g, True) for m, g in BT_CASES]
 
 
 def loop_blocks(text, split_asm_labels=False):
@@ -89,9 +93,9 @@ def expected_loops(mode):
     return 6 if mode == 2 else 3
 
 
-@pytest.mark.parametrize("mode,grouped", CASES)
-def test_main_loop_is_one_block_without_copies(asm, mode, grouped):
-    loops = loop_blocks(kernel_lines(asm, mode, grouped))
+@pytest.mark.parametrize("mode,grouped,bt", ALL_CASES)
+def test_main_loop_is_one_block_without_copies(asm, mode, grouped, bt):
+    loops = loop_blocks(kernel_lines(asm, mode, grouped, bt))
     assert len(loops) == expected_loops(mode), "the 16 x 16 MFMAs of a trip sit in more than one basic block"
     for body in loops:
         mfma = sum(1 for x in body if x.startswith("v_mfma_f32_16x16x32_bf16"))
@@ -106,12 +110,12 @@ def test_main_loop_is_one_block_without_copies(asm, mode, grouped):
     assert sum(1 for body in loops if sum(1 for x in body if x.startswith("v_mfma")) == 256) == expected_loops(mode) // 3
 
 
-@pytest.mark.parametrize("mode,grouped", CASES)
-def test_main_loop_has_no_claim_branch_or_exec_write(asm, mode, grouped):
+@pytest.mark.parametrize("mode,grouped,bt", ALL_CASES)
+def test_main_loop_has_no_claim_branch_or_exec_write(asm, mode, grouped, bt):
     """A branch or an EXEC write inside a k-step holds the wave until the MFMAs in
     flight drain (measured 70-90 cycles per step), so a trip's only branch is its
     back edge and nothing in it writes EXEC or sends an atomic."""
-    loops = loop_blocks(kernel_lines(asm, mode, grouped), split_asm_labels=True)
+    loops = loop_blocks(kernel_lines(asm, mode, grouped, bt), split_asm_labels=True)
     assert len(loops) == expected_loops(mode)
     for body in loops:
         # the trip ends at its back edge (the block's text may run on past it)
@@ -123,9 +127,9 @@ def test_main_loop_has_no_claim_branch_or_exec_write(asm, mode, grouped):
         assert not [x for x in body if x.startswith(("global_atomic", "buffer_atomic", "flat_atomic"))]
 
 
-@pytest.mark.parametrize("mode,grouped", CASES)
-def test_mfma_hazard_distances(asm, mode, grouped):
-    f = instructions(kernel_lines(asm, mode, grouped))
+@pytest.mark.parametrize("mode,grouped,bt", ALL_CASES)
+def test_mfma_hazard_distances(asm, mode, grouped, bt):
+    f = instructions(kernel_lines(asm, mode, grouped, bt))
     mf = [n for n, x in enumerate(f) if x.startswith("v_mfma")]
     # VALU write -> MFMA operand read, over the loop and its back edge
     body = f[mf[0] - 64: mf[-1] + 32] * 2
@@ -171,15 +175,15 @@ def test_mfma_hazard_distances(asm, mode, grouped):
     assert worst is None or worst >= MIN_MFMA_RESULT_DISTANCE, worst
 
 
-@pytest.mark.parametrize("mode,grouped", CASES)
-def test_fast_trips_compute_no_load_masks(asm, mode, grouped):
+@pytest.mark.parametrize("mode,grouped,bt", ALL_CASES)
+def test_fast_trips_compute_no_load_masks(asm, mode, grouped, bt):
     """Vector instructions interleaved with the MFMAs stall them (recomputing the load masks every
     k-step cost about 220 cycles per step; the LDS read address adds about 80 more), so the
     four-step trips, whose stages are compile-time constants, hold no vector instruction besides
     the MFMAs, and the two-step trips with precomputed load offsets at most 24 (the K-tail trips
     carry about 56)."""
     valu = []
-    for body in loop_blocks(kernel_lines(asm, mode, grouped)):
+    for body in loop_blocks(kernel_lines(asm, mode, grouped, bt)):
         ends = [n for n, x in enumerate(body) if x.startswith(("s_cbranch", "s_branch"))]
         body = body[: ends[0] + 1]
         mfma = sum(1 for x in body if x.startswith("v_mfma"))
