@@ -403,7 +403,9 @@ def main():
             modes[name] = {"ms": m_ms, "tflops": flops / (m_ms * 1e-3) / 1e12,
                            "frac_peak": flops / (m_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         for name, mode, pl in runs:
-            ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream)
+            # the log holds the last run: three back to back, so that it is not a first launch after a pause
+            for _ in range(3):
+                ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream)
             mk = makespan_from_log(ptg.gemm_read_log(pl), khz) if not args.no_log else None
             if mk:
                 modes[name].update(makespan_us=mk["makespan_us"], tile_median_us=mk["tile_median_us"])
