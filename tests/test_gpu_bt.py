@@ -102,6 +102,13 @@ def test_bt_operand_shapes_checked():
     A = torch.zeros((16, 24), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         ptg.gemm_run(A, torch.zeros((24, 16), dtype=torch.bfloat16, device="cuda"), new_c(16, 16), plan)  # K x N given
+    # K == 0: C is all zeros in every mode
+    for mode in MODES:
+        C = new_c(300, 264)
+        ptg.gemm_run(torch.zeros((300, 0), dtype=torch.bfloat16, device="cuda"),
+                     torch.zeros((264, 0), dtype=torch.bfloat16, device="cuda"), C, plan, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(C).item() == 0 and not torch.isnan(C).any().item()
     plan.destroy()
     with pytest.raises(ptg.PtgError):
         ptg.gemm_create(tile_edge=256, b_layout=2)
