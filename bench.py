@@ -189,8 +189,11 @@ def run_tail_sections(ptg, torch, stream, khz, square):
     ks = np.array([q.K for q in w.problems])
     # the dynamic scheduler handing out the longest-K problems first, beside the three modes
     lplan = ptg.gemm_create(tile_edge=256, log_capacity=1024, group_order=1)
+    # the same order dealt to contiguous XCD regions (each XCD runs whole problems)
+    cplan = ptg.gemm_create(tile_edge=256, log_capacity=1024, group_order=1, claim_policy=2)
     variants = {mode: (mode, plan) for mode in modes}
     variants["dynamic_longest_k_first"] = ("dynamic", lplan)
+    variants["dynamic_longest_k_first_contiguous_regions"] = ("dynamic", cplan)
     fns = {name: (lambda mode=mode, pl=pl: ptg.gemm_run_grouped(As, Bs, Cs, pl, mode=mode, stream=stream))
            for name, (mode, pl) in variants.items()}
     kernel_ms = time_interleaved(fns, rounds=4, per_round=5, stream=stream)
@@ -211,6 +214,7 @@ def run_tail_sections(ptg, torch, stream, khz, square):
             alpha, beta = np.polyfit(kt, dur, 1)
     res["cost_fit_us"] = {"per_kstep": float(alpha), "fixed": float(beta)}
     lplan.destroy()
+    cplan.destroy()
     res["dynamic_beats_static"] = bool(res["dynamic"]["makespan_us"] < res["static"]["makespan_us"])
     out["grouped_uneven"] = res
     plan.destroy()

@@ -112,9 +112,15 @@ typedef enum gemm_sched_mode {
  *                   x, handed out by counter x; a worker claims from the region
  *                   of the XCD it runs on and, when that is exhausted, steals
  *                   from the other regions. Every tile still has one owner; a
- *                   worker's own-region tiles keep their L2 locality. The
- *                   failure-forcing preset (gemm_test_preset_counter) applies
- *                   to policy 0 only.
+ *                   worker's own-region tiles keep their L2 locality.
+ *                   2 = XCD-partitioned with contiguous regions: region x is
+ *                   the x-th of eight consecutive runs of work-unit ids (in
+ *                   claim order; the first U mod 8 runs one id longer), with
+ *                   the same own-region-first claiming and stealing. Meant for
+ *                   grouped runs of small problems, where it keeps each
+ *                   problem's tiles, and so its A and B panels, on one XCD.
+ *                   The failure-forcing preset (gemm_test_preset_counter)
+ *                   applies to policy 0 only.
  *   raster          0 = row-major tile order; 1 = grouped-M with group height
  *                   raster_group tile rows.
  *   static_workers  static mode's P; 0 = resident workgroups (occupancy x CUs).
@@ -135,7 +141,11 @@ typedef enum gemm_sched_mode {
  *                   longest K first (stable for equal K): a tile's cost grows
  *                   with its K, and handing out the costly tiles first leaves
  *                   the cheap ones to fill the end of the run (the longest-
- *                   processing-time rule). Tile ids in the log keep the
+ *                   processing-time rule). With claim_policy 2 the sorted
+ *                   problems are dealt to the eight regions in snake order
+ *                   (regions 0..7, then 7..0, ...), the regions' lists placed
+ *                   one after another, so every region starts with its share
+ *                   of the longest problems. Tile ids in the log keep the
  *                   as-given numbering either way; unit ids follow the order.
  *   claim_group     single GEMMs only: tiles per work unit (0 or 1 = one tile;
  *                   up to GEMM_MAX_CLAIM_GROUP). One claim (one static step,

@@ -19,8 +19,11 @@ any worker finished that tile. The rules:
 * Dynamic: any exactly-once owner map is valid (the claim order decides it);
   because claims come from one monotone counter each worker's tiles are
   strictly increasing in both id and start time. When tile ids are handed out
-  by several counters, one per region of ids (tile mod `regions`), the ids a
-  worker takes from any one region are strictly increasing.
+  by several counters, one per region of ids, the ids a worker takes from any
+  one region are strictly increasing. Regions are interleaved (region r holds
+  the ids k with k mod `regions` == r) or contiguous (region r holds the r-th
+  of `regions` consecutive runs of ids, the first T mod `regions` runs one
+  id longer than the rest).
 
 Timestamps are taken on the GPU's constant-rate clock; makespan = latest tile
 end - earliest tile start over the tiles that ran.
@@ -39,7 +42,7 @@ from typing import Dict, Iterable, List, Optional
 
 import numpy as np
 
-__all__ = ["check_ownership", "check_k_cover", "split_units", "makespan", "per_worker"]
+__all__ = ["check_ownership", "check_k_cover", "split_units", "makespan", "per_worker", "region_of"]
 
 
 def per_worker(worker: np.ndarray, tiles: np.ndarray) -> Dict[int, np.ndarray]:
@@ -55,9 +58,22 @@ def makespan(start: np.ndarray, end: np.ndarray) -> float:
     return float(np.max(end) - np.min(start))
 
 
+def region_of(tile: np.ndarray, T: int, regions: int, layout: str = "interleaved") -> np.ndarray:
+    """Region of each id under the interleaved or the contiguous layout."""
+    tile = np.asarray(tile, dtype=np.int64)
+    if layout == "interleaved":
+        return tile % regions
+    if layout != "contiguous":
+        raise ValueError(f"unknown region layout {layout}")
+    sizes = [T // regions + (1 if r < T % regions else 0) for r in range(regions)]
+    ends = np.cumsum(sizes)
+    return np.searchsorted(ends, tile, side="right")
+
+
 def check_ownership(mode: str, T: int, tile: np.ndarray, worker: np.ndarray, start: np.ndarray,
                     end: np.ndarray, visits: np.ndarray, P: Optional[int] = None,
-                    expected_tiles: Optional[Iterable[int]] = None, regions: int = 1) -> List[str]:
+                    expected_tiles: Optional[Iterable[int]] = None, regions: int = 1,
+                    region_layout: str = "interleaved") -> List[str]:
     """Return a list of violations (empty when the log obeys every rule).
 
     ``tile``, ``worker``, ``start``, ``end`` are per-record arrays for the tiles that
@@ -104,8 +120,9 @@ def check_ownership(mode: str, T: int, tile: np.ndarray, worker: np.ndarray, sta
             if len(ks) > 1 and np.any(np.diff(ks) <= 0):
                 errs.append(f"worker {w} tiles not increasing in start order: {ks[:8].tolist()}")
         elif mode == "dynamic":
+            reg = region_of(ks, T, regions, region_layout)
             for r in range(regions):
-                kr = ks[ks % regions == r]
+                kr = ks[reg == r]
                 if len(kr) > 1 and np.any(np.diff(kr) <= 0):
                     errs.append(f"worker {w} tiles of region {r} not increasing: {kr[:8].tolist()}")
     if mode == "nonpersistent":

@@ -237,7 +237,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (!valid_tile(d)) return GEMM_E_UNSUPPORTED;
   if (d.ring_depth < 2 || d.ring_depth > 3) return GEMM_E_INVALID_ARG;
   if (d.claims_ahead < 0 || d.claims_ahead > 2 || d.claims_ahead >= d.ring_depth) return GEMM_E_INVALID_ARG;
-  if (d.claim_lead < 0 || d.claim_policy < 0 || d.claim_policy > 1) return GEMM_E_INVALID_ARG;
+  if (d.claim_lead < 0 || d.claim_policy < 0 || d.claim_policy > 2) return GEMM_E_INVALID_ARG;
   if (d.raster < 0 || d.raster > 1 || (d.raster == 1 && d.raster_group < 1)) return GEMM_E_INVALID_ARG;
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
       d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT || d.group_order < 0 ||
@@ -395,10 +395,23 @@ gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const 
   // costs about K; handing out the costly tiles first keeps the short ones for
   // the end, where they fill the gaps: longest-processing-time order). The table
   // goes to the device in claim order; tile ids keep the call-order numbering.
+  // With contiguous XCD regions (claim policy 2) each region is one run of the
+  // claim order, so the sorted problems are dealt to the eight runs in snake
+  // order (0..7, 7..0, ...): every region starts with its share of the longest
+  // problems and the regions' totals stay close.
   std::vector<KernelProblem> table = probs;
   if (p->desc.group_order == 1) {
     std::stable_sort(table.begin(), table.end(),
                      [](const KernelProblem &a, const KernelProblem &b) { return a.K > b.K; });
+    if (p->desc.claim_policy == 2) {
+      std::vector<KernelProblem> dealt[ptg::kXcdRegions];
+      for (size_t i = 0; i < table.size(); ++i) {
+        const size_t round = i / ptg::kXcdRegions, pos = i % ptg::kXcdRegions;
+        dealt[round % 2 == 0 ? pos : ptg::kXcdRegions - 1 - pos].push_back(table[i]);
+      }
+      table.clear();
+      for (const auto &d : dealt) table.insert(table.end(), d.begin(), d.end());
+    }
     int32_t u = 0;
     for (KernelProblem &q : table) {
       q.unit_start = u;

@@ -129,7 +129,8 @@ __device__ __forceinline__ void interleave() {
 
 // One claim. Single-counter policy: the next value of the device-wide counter
 // (plus the failure-forcing base); any value >= T is a failure. XCD-partitioned
-// policy: region x (tiles 8i + x) is handed out by counter x; a worker claims
+// policies: region x (tiles 8i + x, or the x-th of eight consecutive runs of
+// ids; see region_unit) is handed out by counter x; a worker claims
 // from its own XCD's region first (the tiles its XCD's L2 already holds
 // operands for) and, once that is exhausted, steals from another region. Each
 // counter returns each index once, so every tile still has exactly one owner;
@@ -181,6 +182,14 @@ __device__ __forceinline__ uint32_t lane0_fetch_add(uint32_t *ctr, uint32_t lane
 __device__ __forceinline__ uint32_t region_size(uint32_t T, uint32_t y) {
   return T > y ? (T - y + kXcdRegions - 1) / kXcdRegions : 0u;
 }
+// Id of the i-th unit of region y: interleaved regions (policy 1) hold the ids
+// 8i + y; contiguous regions (policy 2) hold the y-th of eight consecutive runs
+// of ids, of the same sizes (the first T mod 8 runs one longer).
+__device__ __forceinline__ uint32_t region_unit(int policy, uint32_t T, uint32_t y, uint32_t i) {
+  if (policy == 1) return i * (uint32_t)kXcdRegions + y;
+  const uint32_t q = T / (uint32_t)kXcdRegions, r = T % (uint32_t)kXcdRegions;
+  return y * q + (y < r ? y : r) + i;
+}
 __device__ __forceinline__ uint32_t claim_issue(const KernelArgs &a, uint32_t region) {
   uint32_t *ctr = a.claim_policy == 0 ? &a.ctrl->counter : &a.ctrl->xcd_counter[region];
   uint32_t v = 0;
@@ -192,7 +201,7 @@ __device__ __forceinline__ uint32_t claim_resolve(const KernelArgs &a, uint32_t 
   const uint32_t i0 = __builtin_amdgcn_readfirstlane(raw);
   if (a.claim_policy == 0) return i0 + a.counter_base;
   const uint32_t T = (uint32_t)a.T;
-  if (i0 < region_size(T, region)) return i0 * (uint32_t)kXcdRegions + region;
+  if (i0 < region_size(T, region)) return region_unit(a.claim_policy, T, region, i0);
   // lane r < 8 watches region (xcc + r) mod 8
   const uint32_t my_y = (xcc + (lane & 7u)) % (uint32_t)kXcdRegions;
   for (int attempt = 0; attempt < kXcdRegions; ++attempt) {
@@ -208,7 +217,7 @@ __device__ __forceinline__ uint32_t claim_resolve(const KernelArgs &a, uint32_t 
     const uint32_t i = lane0_fetch_add(&a.ctrl->xcd_counter[y], lane);
     if (i < region_size(T, y)) {
       region = y;
-      return i * (uint32_t)kXcdRegions + y;
+      return region_unit(a.claim_policy, T, y, i);
     }
   }
   return T;
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       // answers then came back many microseconds late (8192^3 with 128 x 128
       // tiles: 845 -> 955 TFLOP/s)
       bool open = false;
-      if (args.claim_policy == 1) {
+      if (args.claim_policy != 0) {
         if (lane < (uint32_t)kXcdRegions)
           open = __hip_atomic_load(&args.ctrl->xcd_counter[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                  region_size((uint32_t)T, lane);

@@ -64,7 +64,7 @@ struct KernelArgs {
   int32_t claims_ahead;         // 0, 1 or 2 (< ring_depth)
   int32_t ring_depth;           // 2 or 3
   int32_t claim_lead;           // prefetch claims are issued this many k-steps before a tile ends
-  int32_t claim_policy;         // 0: one global counter; 1: per-XCD counters with stealing
+  int32_t claim_policy;         // 0: one global counter; 1/2: per-XCD counters (interleaved / contiguous regions) with stealing
   int32_t raster_group;         // <= 1: row-major
   uint32_t counter_base;        // added to every claim (failure forcing)
   int32_t max_concurrent;       // 0: no gate

@@ -74,12 +74,14 @@ def check_log(plan, mode, T, P=None, expected_tiles=None, K=None, tiles=None, gr
     log = ptg.gemm_read_log(plan)
     assert len(log) == T, (len(log), T)
     assert np.array_equal(log["unit"], np.arange(T) // group)
-    regions = 8 if int(getattr(plan.desc, "claim_policy", 0)) == 1 else 1
+    policy = int(getattr(plan.desc, "claim_policy", 0))
+    regions = 8 if policy in (1, 2) else 1
+    layout = "contiguous" if policy == 2 else "interleaved"
     if group == 1:
         ran = log[log["visits"] > 0]
         errs = check_ownership(mode, T, ran["unit"], ran["worker"], ran["r0"].astype(np.float64),
                                ran["r1"].astype(np.float64), log["visits"], P=P, expected_tiles=expected_tiles,
-                               regions=regions)
+                               regions=regions, region_layout=layout)
         assert not errs, errs
     else:
         # every item once; a unit's items run on one worker, back to back, in item order
@@ -94,7 +96,7 @@ def check_log(plan, mode, T, P=None, expected_tiles=None, K=None, tiles=None, gr
             assert np.all(it["r0"][1:] >= it["r1"][:-1]), u
             worker[u], start[u], end[u] = it["worker"][0], it["r0"][0], it["r1"][-1]
         errs = check_ownership(mode, U, np.arange(U), worker, start, end, np.ones(U, dtype=np.int64), P=P,
-                               regions=regions)
+                               regions=regions, region_layout=layout)
         assert not errs, errs
     if K is not None:
         ran = log[log["visits"] > 0]

@@ -2,7 +2,9 @@
 
 The log's unit -> tile map must equal oracle.sched_model.lpt_claim_order, every
 unit runs exactly once under each scheduler's ownership rule, each tile covers
-its own problem's K exactly once, and every C_g matches the oracle.
+its own problem's K exactly once, and every C_g matches the oracle. With
+contiguous XCD regions (claim_policy = 2) the sorted problems are dealt to the
+eight regions in snake order, and the log must show that order instead.
 """
 
 import numpy as np
@@ -72,3 +74,57 @@ def test_lpt_order_grouped_uneven_workload():
             rows = sorted(set(rng.integers(0, 1024, size=6).tolist() + [0, 1023]))
             assert_close_rows(w.problems[g], cs[g], rows)
     plan.destroy()
+
+
+def _dealt_order(ks, tiles, regions=8):
+    """Tile ids in claim order: problems by descending K (stable), dealt to the
+    regions 0..7, 7..0, 0..7, ..., the regions' lists concatenated."""
+    order = sorted(range(len(ks)), key=lambda g: -ks[g])
+    dealt = [[] for _ in range(regions)]
+    for i, g in enumerate(order):
+        rnd, pos = divmod(i, regions)
+        dealt[pos if rnd % 2 == 0 else regions - 1 - pos].append(g)
+    starts = np.cumsum([0] + list(tiles))
+    return [t for lst in dealt for g in lst for t in range(starts[g], starts[g + 1])]
+
+
+def test_lpt_dealt_to_contiguous_regions():
+    w = make_workload("grouped_uneven")
+    ks = [q.K for q in w.problems]
+    plan = ptg.gemm_create(tile_edge=256, log_capacity=1024, group_order=1, claim_policy=2)
+    want = _dealt_order(ks, [16] * 64)
+    assert sorted(want) == list(range(1024))
+    # each region (128 units) holds eight whole problems; with the snake deal the
+    # regions' K sums differ by at most max K - min K
+    sums = [sum(ks[want[r * 128 + 16 * j] // 16] for j in range(8)) for r in range(8)]
+    assert max(sums) - min(sums) <= max(ks) - min(ks)
+    rng = np.random.default_rng(11)
+    for mode in MODES:
+        say(f"case lpt dealt grouped_uneven policy=2 mode={mode}")
+        cs = _run_grouped(w.problems, plan, mode)
+        info = ptg.gemm_plan_info_get(plan)
+        log = check_log(plan, mode, 1024, P=info["last_grid"] if mode == "static" else None,
+                        K=_tile_k(w.problems, 256))
+        assert log["tile"].tolist() == want
+        for g in range(3, 64, 10):
+            rows = sorted(set(rng.integers(0, 1024, size=6).tolist() + [0, 1023]))
+            assert_close_rows(w.problems[g], cs[g], rows)
+    plan.destroy()
+
+
+def test_contiguous_regions_small_ragged_problems():
+    # 21 tiles over 8 regions (five of 3 ids, three of 2): regions cut through problems
+    shapes = [(300, 264, 520), (128, 520, 1000), (700, 256, 64), (256, 136, 1000), (1, 8, 8), (513, 704, 96)]
+    problems = [make_problem(M, N, K, "uniform", seed=20 + i) for i, (M, N, K) in enumerate(shapes)]
+    tiles = [-(-M // 256) * -(-N // 256) for M, N, _ in shapes]
+    T = sum(tiles)
+    for order in (0, 1):
+        plan = make_plan(256, group_order=order, claim_policy=2)
+        want = _dealt_order([q.K for q in problems], tiles) if order == 1 else list(range(T))
+        say(f"case contiguous regions small ragged T={T} group_order={order}")
+        cs = _run_grouped(problems, plan, "dynamic")
+        for q, c in zip(problems, cs):
+            assert_close_full(q, c)
+        log = check_log(plan, "dynamic", T, K=_tile_k(problems, 256))
+        assert log["tile"].tolist() == want
+        plan.destroy()

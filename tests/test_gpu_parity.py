@@ -125,7 +125,7 @@ def test_empty_and_degenerate_inputs():
 
 def test_plan_validation():
     for bad in ({"tile_edge": 256, "claims_ahead": 3}, {"tile_edge": 256, "ring_depth": 4},
-                {"tile_edge": 256, "claim_policy": 2}, {"tile_edge": 256, "claim_lead": -1},
+                {"tile_edge": 256, "claim_policy": 3}, {"tile_edge": 256, "claim_lead": -1},
                 {"tile_edge": 256, "ring_depth": 2, "claims_ahead": 2}, {"tile_edge": 256, "raster": 2},
                 {"tile_edge": 256, "device": 99}):
         with pytest.raises(ptg.PtgError):
@@ -142,7 +142,7 @@ def test_plan_validation():
     plan.destroy()
 
 
-@pytest.mark.parametrize("policy", [0, 1])
+@pytest.mark.parametrize("policy", [0, 1, 2])
 @pytest.mark.parametrize("q,depth", [(0, 3), (1, 3), (2, 3), (1, 2), (0, 2)])
 def test_claims_ahead_variants(q, depth, policy):
     p = make_problem(1280, 1024, 512, "uniform", seed=q * 10 + depth)
@@ -221,15 +221,17 @@ def test_failure_forcing_counter_preset():
     plan.destroy()
 
 
+@pytest.mark.parametrize("policy", [1, 2])
 @pytest.mark.parametrize("shape,cap", [((1280, 1024, 128), 1), ((768, 768, 64), 2), ((256, 512, 64), 1)])
-def test_xcd_regions_drained_by_stealing(shape, cap):
-    # with at most `cap` workers alive, the few workers must drain every XCD region,
-    # most of them by stealing; T = 20, 9 and 2 leave some regions empty or uneven
+def test_xcd_regions_drained_by_stealing(shape, cap, policy):
+    # with at most `cap` workers alive, the few workers must drain every XCD region
+    # (interleaved or contiguous), most of them by stealing; T = 20, 9 and 2 leave
+    # some regions empty or uneven
     M, N, K = shape
     p = make_problem(M, N, K, "uniform", seed=M + cap)
-    plan = make_plan(256, claim_policy=1, max_concurrent=cap, min_lds_bytes=96 * 1024)
+    plan = make_plan(256, claim_policy=policy, max_concurrent=cap, min_lds_bytes=96 * 1024)
     T = -(-M // 256) * -(-N // 256)
-    say(f"case xcd stealing shape={shape} cap={cap} T={T}")
+    say(f"case xcd stealing shape={shape} cap={cap} T={T} policy={policy}")
     c = run(p, plan, "dynamic")
     assert_close_full(p, c)
     log = check_log(plan, "dynamic", T)

@@ -123,7 +123,7 @@ def test_split_result_close_to_whole_tiles():
     b.destroy()
 
 
-@pytest.mark.parametrize("tile,q,policy", [(256, 0, 1), (256, 2, 0), (128, 1, 1), (128, 2, 1)])
+@pytest.mark.parametrize("tile,q,policy", [(256, 0, 1), (256, 2, 0), (256, 1, 2), (128, 1, 1), (128, 2, 1)])
 def test_tail_split_with_claim_options(tile, q, policy):
     # the split tail under other claim settings and the 128 tile: T = workers + 3 tiles
     torch = __import__("torch")

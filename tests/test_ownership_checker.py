@@ -63,6 +63,27 @@ def test_region_rule_for_partitioned_claims():
     assert check_ownership("dynamic", 5, bad, worker, start, end, visits, regions=2)
 
 
+def test_region_rule_for_contiguous_regions():
+    # T = 5 in two contiguous regions {0, 1, 2} and {3, 4}: a worker that drains
+    # region 1 and then steals region 0 from its start is valid; the same order
+    # breaks the interleaved rule ({0, 2, 4}: 4 before 0) and the one-counter rule
+    from oracle.ownership import region_of
+    assert region_of(np.arange(5), 5, 2, "contiguous").tolist() == [0, 0, 0, 1, 1]
+    assert region_of(np.arange(10), 10, 4, "contiguous").tolist() == [0, 0, 0, 1, 1, 1, 2, 2, 3, 3]
+    assert region_of(np.arange(3), 3, 8, "contiguous").tolist() == [0, 1, 2]
+    tile = np.array([3, 4, 0, 1, 2])
+    worker = np.zeros(5, dtype=np.int64)
+    start = np.arange(5, dtype=float)
+    end = start + 1
+    visits = np.ones(5, dtype=np.int64)
+    assert not check_ownership("dynamic", 5, tile, worker, start, end, visits, regions=2,
+                               region_layout="contiguous")
+    assert check_ownership("dynamic", 5, tile, worker, start, end, visits, regions=2)
+    assert check_ownership("dynamic", 5, tile, worker, start, end, visits)
+    bad = np.array([4, 3, 0, 1, 2])                                                    # region 1 out of order
+    assert check_ownership("dynamic", 5, bad, worker, start, end, visits, regions=2, region_layout="contiguous")
+
+
 def test_k_cover_accepts_partitions_and_rejects_planted_errors():
     from oracle.ownership import check_k_cover
     # three whole tiles and tile 3 cut into chunks [0,128) [128,320) [320,512)
