@@ -19,16 +19,18 @@ pytestmark = pytest.mark.gpu
 MODES = ("nonpersistent", "static", "dynamic")
 
 
-@pytest.mark.parametrize("group,raster", [(2, 0), (4, 2), (3, 0)])
-def test_claim_groups_all_modes(group, raster):
+@pytest.mark.parametrize("group,raster,policy", [(2, 0, 1), (4, 2, 1), (3, 0, 1), (3, 0, 2), (4, 2, 0)])
+def test_claim_groups_all_modes(group, raster, policy):
+    # claim policies 1 and 2 spread the units over eight XCD regions (interleaved
+    # or contiguous runs of unit ids), policy 0 hands them out from one counter
     M, N, K = 1800, 1288, 200      # 8 x 6 = 48 tiles of 256, ragged M, N and K
     p = make_problem(M, N, K, "uniform", seed=group)
     kw = {"raster": 1, "raster_group": raster} if raster else {}
-    plan = make_plan(256, claim_group=group, **kw)
+    plan = make_plan(256, claim_group=group, claim_policy=policy, **kw)
     ref = make_plan(256, **kw)
     T = 48
     for mode in MODES:
-        say(f"case claim group={group} raster={raster} mode={mode}")
+        say(f"case claim group={group} raster={raster} policy={policy} mode={mode}")
         c = run(p, plan, mode)
         assert_close_full(p, c)
         info = ptg.gemm_plan_info_get(plan)
