@@ -315,8 +315,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the single-GPU path is what is measured; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(only the single-GPU path is measured).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -398,7 +398,7 @@ def main():
             torch.mm(A, B, out_dtype=torch.float32)
             torch.cuda.synchronize()
             fns["vendor_mm_fp32_out"] = lambda: torch.mm(A, B, out_dtype=torch.float32)
-        except Exception as e:  # not offered by this build: reported as absent (context only)
+        except Exception as e:  # not offered by the installed torch: reported as absent (context only)
             log(f"vendor fp32-output mm unavailable: {e}")
         # the clock drifts over tens of milliseconds under this load, so the variants are timed in
         # interleaved blocks (alternating order), not one after another
