@@ -299,8 +299,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--mode", default="dynamic", choices=["nonpersistent", "static", "dynamic"])
     ap.add_argument("--claims-ahead", type=int, default=1)
-    ap.add_argument("--claim-policy", type=int, default=1, choices=[0, 1],
-                    help="0: one device-wide claim counter; 1: per-XCD counters with stealing")
+    ap.add_argument("--claim-policy", type=int, default=1, choices=[0, 1, 2],
+                    help="0: one device-wide claim counter; 1: per-XCD counters with stealing (interleaved "
+                         "regions); 2: the same with contiguous regions (the 8192^3 line takes 0 or 1)")
+    ap.add_argument("--group-order", type=int, default=0, choices=[0, 1],
+                    help="grouped workloads under --profile-workload: 1 = longest K first")
     ap.add_argument("--raster-group", type=int, default=0, help="grouped-M raster height (0: row-major)")
     ap.add_argument("--no-log", action="store_true", help="turn the tile log off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -309,10 +312,12 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) to scale the HBM byte counters")
     ap.add_argument("--profile-workload", default="", metavar="NAME",
-                    choices=["", "tail_255", "tail_256", "tail_257"],
-                    help="only run that single-GEMM workload (--steps times, after --warmup) for a profiler; "
+                    choices=["", "tail_255", "tail_256", "tail_257", "grouped_uneven"],
+                    help="only run that workload (--steps times, after --warmup) for a profiler; "
                          "prints its timing and algorithmic HBM rate, not the benchmark line")
     args = ap.parse_args()
+    if args.claim_policy == 2 and not args.profile_workload:
+        ap.error("--claim-policy 2 applies to --profile-workload runs only")
 
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -324,19 +329,25 @@ def main():
         import persistent_tiled_gemm_amd as ptg
         from workloads import make_workload
         ptg.load_library()
-        q = make_workload(args.profile_workload).problems[0]
-        A = ptg.bf16_from_bits(q.a_bits)
-        B = ptg.bf16_from_bits(q.b_bits)
-        C = torch.empty((q.M, q.N), dtype=torch.float32, device="cuda")
-        plan = ptg.gemm_create(tile_edge=256, claim_policy=args.claim_policy, log_capacity=0 if args.no_log else 512)
+        probs = make_workload(args.profile_workload).problems
+        As = [ptg.bf16_from_bits(q.a_bits) for q in probs]
+        Bs = [ptg.bf16_from_bits(q.b_bits) for q in probs]
+        Cs = [torch.empty((q.M, q.N), dtype=torch.float32, device="cuda") for q in probs]
+        plan = ptg.gemm_create(tile_edge=256, claim_policy=args.claim_policy, group_order=args.group_order,
+                               log_capacity=0 if args.no_log else 1024)
         stream = torch.cuda.current_stream()
-        ms = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=args.mode, stream=stream), args.steps, args.warmup,
-                       stream)
-        nbytes = q.M * q.K * 2 + q.K * q.N * 2 + q.M * q.N * 4
-        print(json.dumps({"workload": args.profile_workload, "mode": args.mode, "ms": ms,
+        if len(probs) == 1:
+            fn = lambda: ptg.gemm_run(As[0], Bs[0], Cs[0], plan, mode=args.mode, stream=stream)
+        else:
+            fn = lambda: ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=args.mode, stream=stream)
+        ms = time_runs(fn, args.steps, args.warmup, stream)
+        nbytes = sum(q.M * q.K * 2 + q.K * q.N * 2 + q.M * q.N * 4 for q in probs)
+        flops = sum(2.0 * q.M * q.N * q.K for q in probs)
+        print(json.dumps({"workload": args.profile_workload, "mode": args.mode, "claim_policy": args.claim_policy,
+                          "group_order": args.group_order, "ms": ms,
                           "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / (ms * 1e-3) / 1e9,
                           "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                          "tflops": 2.0 * q.M * q.N * q.K / (ms * 1e-3) / 1e12}), flush=True)
+                          "tflops": flops / (ms * 1e-3) / 1e12}), flush=True)
         plan.destroy()
         return
     if args.calibrate_copy > 0:
