@@ -247,7 +247,12 @@ def gemm_run_raw(A_ptr: int, B_ptr: int, C_ptr: int, M: int, N: int, K: int, pla
 
 
 def gemm_run_grouped(As: Sequence, Bs: Sequence, Cs: Sequence, plan: Plan, mode="dynamic", stream=None) -> None:
-    """gemm_run_grouped: all problems C_g = A_g.B_g in one launch."""
+    """gemm_run_grouped: all problems C_g = A_g.B_g in one launch.
+
+    For many small problems of uneven K, a plan made with group_order=1 (longest
+    K first) and claim_policy=2 (contiguous XCD regions, so each XCD runs whole
+    problems and shares their operand panels in its own L2) gave the shortest
+    dynamic makespan measured on 64 problems of 1024 x 1024 with K from 512 to 8192."""
     G = len(As)
     if not (len(Bs) == len(Cs) == G) or G == 0:
         raise ValueError("need equally many A, B, C (at least one)")
