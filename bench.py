@@ -105,6 +105,17 @@ def makespan_from_log(rec, khz):
             "workers": int(len(np.unique(ran["worker"]))), "cus": int(len(np.unique(cu_key(ran["hw_id"], ran["xcc_id"]))))}
 
 
+def clock_from_log(rec, khz):
+    """Mean shader clock (GHz) over the logged items of a run: s_memtime cycles over s_memrealtime ticks."""
+    ran = rec[rec["visits"] > 0]
+    if len(ran) == 0:
+        return None
+    cyc = (ran["t1"] - ran["t0"]).astype(np.float64)
+    wall = (ran["r1"] - ran["r0"]).astype(np.float64)
+    ok = wall > 0
+    return float(np.sum(cyc[ok]) / np.sum(wall[ok]) * khz * 1e-6)
+
+
 def median_run(run_and_read, khz, n: int = 3):
     """Call run_and_read() n times (it runs one launch, waits for it and returns (log records, extra
     fields)); return the makespan summary of the run with the median makespan, with every run's
@@ -121,14 +132,47 @@ def median_run(run_and_read, khz, n: int = 3):
     return ms, rec
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def blas_info():
+    """(threads, vendor string) of the BLAS numpy calls: threadpoolctl's view of the loaded library,
+    else numpy's build configuration."""
+    threads, vendor = None, None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            threads = max(int(i.get("num_threads", 1)) for i in blas)
+            vendor = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '?')} "
+                               f"threading, {i.get('architecture', '?')})" for i in blas)
+    except Exception:  # pragma: no cover
+        pass
+    if vendor is None:
+        try:
+            cfg = np.show_config(mode="dicts")
+            b = cfg["Build Dependencies"]["blas"]
+            vendor = f"{b.get('name')} {b.get('version')}"
+        except Exception:  # pragma: no cover
+            vendor = "unknown"
+    return threads, vendor
+
+
 def cpu_baseline(problem, target_s: float = 10.0):
     """Time the CPU oracle (gemm_ref_rows: exact bf16 decode + fp64 product) on a row sample."""
     from oracle.gemm_ref import gemm_ref_rows
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads, vendor = blas_info()
+    affinity = len(os.sched_getaffinity(0))
+    if threads is None:
+        threads = affinity
     M, K = problem.a_bits.shape
     N = problem.b_bits.shape[1]
     rows = 256
@@ -141,7 +185,10 @@ def cpu_baseline(problem, target_s: float = 10.0):
     t = time.perf_counter() - t0
     flops = 2.0 * rows * N * K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} of {M} rows of C (all {N} columns, K={K}), fp64, {t:.2f} s"}
+            "sample": f"first {rows} of {M} rows of C (all {N} columns, K={K}), fp64, {t:.2f} s",
+            "cores_note": "BLAS threads the fp64 product ran on (the decode is single-threaded NumPy)",
+            "affinity_cpus": affinity, "blas": vendor, "cpu_model": host_cpu_model(),
+            "fp64_gflops": flops / t / 1e9, "wall_s": t}
 
 
 def run_tail_sections(ptg, torch, stream, khz, square):
@@ -158,7 +205,7 @@ def run_tail_sections(ptg, torch, stream, khz, square):
     res = {}
     def co_run(mode):
         spoiler_log = torch.zeros(64 * 4, dtype=torch.int64, device="cuda")
-        ptg.gemm_spoiler_run(64, 2_000_000, stream=spoil_stream, log=spoiler_log, wait_resident_ms=2000.0)
+        ptg.gemm_test_spoiler(64, 2_000_000, stream=spoil_stream, log=spoiler_log, wait_resident_ms=2000.0)
         ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
         torch.cuda.synchronize()
         rec = ptg.gemm_read_log(plan)
@@ -278,14 +325,33 @@ def run_tail_sections(ptg, torch, stream, khz, square):
         ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
         torch.cuda.synchronize()
         return ptg.gemm_read_log(plan), {}
+    we_logs = {}
     for mode in modes:
         for _ in range(2):
             ptg.gemm_run(A, B, C, plan, mode=mode, stream=stream)
-        res[mode], _ = median_run(lambda: logged_we(mode), khz, n=5)
+        res[mode], we_logs[mode] = median_run(lambda: logged_we(mode), khz, n=5)
     # makespan in units of each mode's own median tile time (the pages' t)
     for mode in modes:
         res[mode]["makespan_t"] = res[mode]["makespan_us"] / res[mode]["tile_median_us"]
     res["static_over_dynamic"] = res["static"]["makespan_us"] / res["dynamic"]["makespan_us"]
+    # the two overheads the pages' hand calculation leaves out, from the logs of the median runs:
+    # the gate handoff (non-persistent: the (k+3)-th start follows the k-th end) and the exposed
+    # per-tile claim cost (dynamic: gaps between a worker's consecutive tiles)
+    np_rec, dyn_rec = we_logs["nonpersistent"], we_logs["dynamic"]
+    r0 = np.sort(np_rec["r0"].astype(np.float64))
+    r1 = np.sort(np_rec["r1"].astype(np.float64))
+    handoff_us = float(np.median((r0[3:] - r1[:-3]) / khz * 1e3))
+    gaps = []
+    for w in np.unique(dyn_rec["worker"]):
+        mine = dyn_rec[dyn_rec["worker"] == w]
+        mine = mine[np.argsort(mine["r0"])]
+        gaps += ((mine["r0"][1:].astype(np.float64) - mine["r1"][:-1].astype(np.float64)) / khz * 1e3).tolist()
+    claim_gap_us = float(np.median(gaps)) if gaps else 0.0
+    res["overheads_us"] = {"gate_handoff_l": handoff_us, "claim_gap_k": claim_gap_us}
+    t_np, t_st, t_dy = (res[m]["tile_median_us"] for m in ("nonpersistent", "static", "dynamic"))
+    res["with_overheads_t"] = {"nonpersistent": (4 * t_np + 3 * handoff_us) / t_np,
+                               "static": (6 * t_st + handoff_us) / t_st,
+                               "dynamic": (4 * t_dy + 3 * claim_gap_us) / t_dy}
     res["pages_hand_calc_t"] = {"static": 6, "dynamic": 4, "nonpersistent": 4}
     out["worked_example"] = res
     plan.destroy()
@@ -386,6 +452,7 @@ def main():
     log(f"timing {args.mode}: warmup {args.warmup}, steps {args.steps}")
     ms = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=args.mode, stream=stream), args.steps, args.warmup, stream)
     tflops = flops / (ms * 1e-3) / 1e12
+    clock_ghz = None if args.no_log else clock_from_log(ptg.gemm_read_log(plan), khz)
 
     modes = {}
     if not args.no_modes:
@@ -433,6 +500,11 @@ def main():
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(1.0),
             "kernel": f"ptg_gemm_kernel<256,256,{args.mode}>", "avg_launch_ms": ms,
             "algorithmic_flop_per_launch": flops}
+    if clock_ghz:
+        # the dense bf16 rate at the clock the GEMM itself ran at (256 CUs x 4096 flop per clock)
+        peak_at_clock = info["cu_count"] * 4096 * clock_ghz * 1e-3
+        roof.update(clock_ghz=clock_ghz, peak_at_clock=peak_at_clock, frac_at_clock=tflops / peak_at_clock,
+                    clock_source="tile log of the last timed launch: s_memtime cycles / s_memrealtime ticks")
 
     out = {"metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",

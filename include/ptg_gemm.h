@@ -15,13 +15,25 @@
  *   GEMM_SCHED_STATIC         grid = P workers; worker i computes i, i+P, i+2P, ...
  *                             (section "why a fixed task sequence tails").
  *   GEMM_SCHED_DYNAMIC        grid = all tiles (launch slots); every workgroup takes
- *                             tiles from one device-wide atomic claim counter, the
- *                             claim of the next tile is prefetched through a ring of
- *                             response records in LDS (depth 3), a failed claim ends
- *                             the worker, late-launched slots exit after one failed
- *                             claim. This replaces the hardware launch-cancel of the
- *                             blog post (sections "cancelling the launch ..." and
- *                             "following the CUTLASS source"), which gfx950 lacks.
+ *                             tiles from atomic claim counters, the claim of the next
+ *                             tile is prefetched through a ring of response records in
+ *                             LDS (depth 3), a failed claim ends the worker,
+ *                             late-launched slots exit after one failed claim. This
+ *                             replaces the hardware launch-cancel of the blog post
+ *                             (sections "cancelling the launch ..." and "following
+ *                             the CUTLASS source"), which gfx950 lacks.
+ *
+ * Claim counters of the dynamic mode (plan field claim_policy):
+ *   0  one device-wide counter hands out every tile id in order: the pages' single
+ *      work queue.
+ *   1  (the default) eight counters, one per XCD: tile ids with id mod 8 == x form
+ *      region x, the set a plain launch sends to XCD x. A worker claims from its
+ *      own XCD's region and steals from the others once that is exhausted. Each
+ *      counter returns each id of its region once, so exactly-once holds as with
+ *      one counter; the worker's own-region tiles keep their operands in its
+ *      XCD's L2 (MI355X has eight L2s; the pages' part has one).
+ *   2  the same with contiguous regions (region x = the x-th of eight consecutive
+ *      runs of ids), for grouped runs of small problems.
  *
  * Tail splitting (optional, tail_split >= 2; single GEMMs only). Whole tiles
  * quantise the finish: T = P + 1 tiles on P workers take two tile times. The
@@ -43,15 +55,19 @@
  *
  * Ownership. The caller owns A, B, C and keeps them alive until the stream has
  * passed the kernel. The plan (gemm_tile_cfg) owns all library scratch: the
- * claim counter, the tile log, the visit counters and the grouped-problem table.
- * Runs are asynchronous and stream-ordered; nothing here synchronises except
- * gemm_read_log and gemm_spoiler_run's optional residency wait. A plan serves
- * one stream at a time and is not thread-safe.
+ * claim counters, the tile log, the visit counters, the device status word and
+ * the grouped-problem table. Runs are asynchronous and stream-ordered; nothing
+ * here synchronises except gemm_sync, gemm_read_log, gemm_destroy and
+ * gemm_test_spoiler's optional residency wait. Runs of one plan on different
+ * streams are ordered on the device (a run waits for the plan's previous
+ * stream). A plan is not thread-safe.
  *
  * Errors. Every call returns a gemm_status; 0 is success. Invalid arguments are
  * rejected before anything is enqueued. HIP failures return GEMM_E_HIP and the
- * HIP error text is kept in the plan (gemm_last_hip_error). Nothing aborts and
- * nothing throws across this boundary.
+ * HIP error text is kept in the plan (gemm_last_hip_error). Failures inside a
+ * kernel (a gate wait that ran out, a ring protocol violation) are kept in the
+ * plan's device status until gemm_sync or gemm_read_log returns them. Nothing
+ * aborts and nothing throws across this boundary.
  */
 #ifndef PTG_GEMM_H
 #define PTG_GEMM_H
@@ -126,8 +142,20 @@ typedef enum gemm_sched_mode {
  *   static_workers  static mode's P; 0 = resident workgroups (occupancy x CUs).
  *   log_capacity    work units to log per run; 0 turns the log off.
  *   min_lds_bytes   dynamic LDS padding per workgroup (limits residency; 0 = none).
- *   max_concurrent  0 = no cap; n > 0 lets at most n workgroups compute at once
- *                   (a device-side gate with a bounded wait).
+ *   max_concurrent  0 = no cap; n > 0 lets at most n workgroups compute at once:
+ *                   the "only 3 workers can run at the same time" condition of
+ *                   the worked example in the blog post's section "why a fixed
+ *                   task sequence tails". Reading taken: a device-side gate (an
+ *                   atomic count of workgroups holding a slot), not a stream whose
+ *                   CU mask leaves 3 compute units: this part sends workgroup w to
+ *                   XCD w mod 8, and a mask that leaves whole XCDs without a CU
+ *                   risks stalling the workgroups sent there. With min_lds_bytes
+ *                   over half the CU's LDS each gated worker also owns its CU.
+ *                   A workgroup waiting at the gate gives up after gate_spin_limit
+ *                   polls; it then computes nothing and sets the plan's device
+ *                   status to GEMM_E_TIMEOUT (gemm_sync, gemm_read_log). In the
+ *                   static and non-persistent modes its tiles are then missing
+ *                   from C; in the dynamic mode the other workers claim them.
  *   max_groups      capacity of the grouped-problem table (0 = 1024).
  *   device          HIP device ordinal; must be gfx950.
  *   tail_split      0 = off. s in 2..GEMM_MAX_TAIL_SPLIT: split each tile of a
@@ -160,6 +188,21 @@ typedef enum gemm_sched_mode {
  *                   C = A . B^T (torch.matmul(A, Bt.T)); its rows are K long,
  *                   so the same K % 8 and N % 8 rules apply. Applies to the
  *                   plan's single and grouped runs alike.
+ *   gate_spin_limit polls of the concurrency gate before a waiting workgroup
+ *                   gives up (0 = the default, about 4 million: a few seconds).
+ *   k_rotation      the order a work unit walks its K range in (the sum is the
+ *                   same; only the fp32 rounding order inside a tile changes,
+ *                   and it depends on the unit id alone, so all schedulers give
+ *                   bitwise the same C). 0 = from the first k-step to the last.
+ *                   1 = rotated: unit u starts at k-step (u mod 8) / 8 of its
+ *                   range and wraps around, so the eight XCD regions walk K at
+ *                   eight different phases while the workgroups of one XCD,
+ *                   which share operand panels through its L2, stay together.
+ *                   2 = rotated by a phase per unit (a hash of its id). Spreading
+ *                   the phases keeps the concurrent reads of all CUs from
+ *                   sharing their low address bits, which holds memory
+ *                   bandwidth well below what the part streams otherwise.
+ *                   Ignored (0) for units whose K is not a multiple of 32.
  */
 typedef struct gemm_tile_desc {
   int32_t bm, bn, bk;
@@ -179,6 +222,8 @@ typedef struct gemm_tile_desc {
   int32_t group_order;
   int32_t claim_group;
   int32_t b_layout;
+  int32_t gate_spin_limit;
+  int32_t k_rotation;
 } gemm_tile_desc;
 
 /* Opaque plan: the tile_cfg argument of gemm_run. Owns all library scratch. */
@@ -224,25 +269,60 @@ typedef struct gemm_plan_info {
   int32_t lds_bytes;         /* LDS per workgroup */
 } gemm_plan_info;
 
-/* Fill *out with the defaults for a square tile edge of 128 or 256 on `device`. */
+/*
+ * Fill *out with the defaults for a square tile edge of 128 or 256 on `device`:
+ * ring depth 3 and one claim ahead (the response pipeline depth and throttle of
+ * the blog post's section "following the CUTLASS source"), per-XCD claim
+ * counters, log off. Errors: GEMM_E_INVALID_ARG (out NULL), GEMM_E_UNSUPPORTED
+ * (another edge). No HIP call.
+ */
 gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t device);
 
-/* Validate *desc and build a plan on desc->device. *out receives the plan. */
+/*
+ * Validate *desc and build a plan on desc->device, which must be the current
+ * device. The plan is the scheduler configuration of the task-scheduling guide
+ * ("CUTLASS Task Scheduling resources", section "TileSchedulerConfig": the
+ * scheduler type and its parameters are fixed before launch) together with all
+ * device scratch a run needs: the claim counters, the tile log and visit
+ * counters, the grouped-problem table and, with tail_split, the partial-sum
+ * workspace. All allocation happens here, none in gemm_run. *out receives the
+ * plan (NULL on failure). Errors: GEMM_E_INVALID_ARG (a field out of range, or
+ * LDS padding beyond the device limit), GEMM_E_UNSUPPORTED (not gfx950 - the
+ * capability check of "B200 Cluster Persistent Scheduler", section "B -
+ * boundaries" - or an unsupported tile), GEMM_E_DEVICE (desc->device is not
+ * current), GEMM_E_NOMEM, GEMM_E_HIP.
+ */
 gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc);
 
 /*
  * Enqueue C = A.B on `stream` (a hipStream_t; NULL = the null stream) with
- * scheduler `sched_mode`. A: M x K bf16, B: K x N bf16, C: M x N fp32, all
+ * scheduler `sched_mode`, one of the three modes of the blog post's table in
+ * the section "from one tile per block to one worker computing continuously"
+ * (see the top of this file). A: M x K bf16, B: K x N bf16, C: M x N fp32, all
  * device pointers. M == 0 or N == 0 enqueues nothing; K == 0 writes zeros.
+ * Exactly one kernel launch; no allocation, no host synchronisation. If the
+ * plan's previous run was enqueued on another stream, the run first waits on
+ * the device for that stream's work (the plan's scratch serves one run at a
+ * time). Errors (returned before anything is enqueued): GEMM_E_INVALID_ARG (a
+ * NULL pointer for a non-empty problem, pointers not 16-byte aligned, a bad
+ * mode), GEMM_E_SHAPE (negative sizes, K or N not a multiple of 8, over a size
+ * limit), GEMM_E_DEVICE (another device is current); GEMM_E_HIP if the launch
+ * fails. Failures inside the kernel are reported later by gemm_sync or
+ * gemm_read_log.
  */
 gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t N, int64_t K,
                      int32_t sched_mode, gemm_tile_cfg tile_cfg, void *stream);
 
 /*
  * Grouped variant: G independent problems C_g = A_g.B_g in one launch, their
- * tiles numbered problem after problem. A, B, C, M, N, K are host arrays of
- * length G (copied before return; the caller may free them). Each problem
- * follows the single-GEMM rules. G <= the plan's max_groups.
+ * tiles numbered problem after problem: the uneven-cost work the "B200 Cluster
+ * Persistent Scheduler" page sends to the dynamic scheduler (section "E -
+ * executable steps", choosing the scheduling mode). A, B, C, M, N, K are host
+ * arrays of length G (copied before return; the caller may free them). Each
+ * problem follows the single-GEMM rules. G <= the plan's max_groups, else
+ * GEMM_E_SHAPE; G <= 0 or a NULL array is GEMM_E_INVALID_ARG. The problem
+ * table is copied to the device on `stream` (from the plan's pinned staging)
+ * only when it differs from the last one.
  */
 gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const *B, float *const *C,
                              const int64_t *M, const int64_t *N, const int64_t *K,
@@ -252,17 +332,33 @@ gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const 
  * Synchronise the last run's stream and copy its log to host_out (up to cap
  * records, in unit-id order, including units that never ran: visits == 0; for
  * those, tile and k_begin/k_end are what the launch planned and worker is
- * 0xFFFFFFFF).
- * *n_out receives the number of records written. Returns GEMM_E_TIMEOUT if a
- * workgroup of the run gave up waiting at the concurrency gate, GEMM_E_SCHED if
- * a consumer found a ring record for the wrong ordinal (the log is still copied).
+ * 0xFFFFFFFF). The log is the per-tile ownership record whose exactly-once
+ * property the blog post's section "cancelling the launch, receiving the work
+ * coordinate" states (each tile owned by one worker). *n_out receives the
+ * number of records written (0 with the log off). Returns the device status as
+ * gemm_sync does, also when the log is off; the log is still copied.
  */
 gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_t cap, size_t *n_out);
+
+/*
+ * Synchronise the plan's last stream and return the device-side status of every
+ * run since the previous gemm_sync or gemm_read_log, then clear it. A failure
+ * must be observable ("CUTLASS Cluster Launch Control dynamic persistent kernel",
+ * section "cluster granularity and exit after failure"): GEMM_E_TIMEOUT if a
+ * workgroup gave up waiting at the concurrency gate (it computed nothing; in
+ * the static and non-persistent modes its tiles are missing from C),
+ * GEMM_E_SCHED if a consumer found a claim-ring record for the wrong ordinal.
+ * GEMM_OK before the first run. GEMM_E_HIP if the synchronisation fails.
+ */
+gemm_status gemm_sync(gemm_tile_cfg tile_cfg);
 
 /* Read plan facts. */
 gemm_status gemm_plan_info_get(gemm_tile_cfg tile_cfg, gemm_plan_info *out);
 
-/* Release the plan and its scratch (synchronises its last stream first). NULL is a no-op. */
+/*
+ * Release the plan and its scratch (synchronises its last stream first). NULL is
+ * a no-op. Device status not yet read is discarded.
+ */
 gemm_status gemm_destroy(gemm_tile_cfg tile_cfg);
 
 /* Static text for a status code. */
@@ -280,6 +376,32 @@ const char *gemm_last_hip_error(gemm_tile_cfg tile_cfg);
 gemm_status gemm_test_preset_counter(gemm_tile_cfg tile_cfg, uint32_t start);
 
 /*
+ * Failure forcing for tests: the next run of a plan with max_concurrent > 0
+ * starts with `held` of its gate slots counted as taken. With held >=
+ * max_concurrent every workgroup's bounded wait runs out (after the plan's
+ * gate_spin_limit polls), every workgroup exits without computing, and
+ * gemm_sync reports GEMM_E_TIMEOUT: the failure path of the blog post's section
+ * "cluster granularity and exit after failure", forced from the host so the
+ * kernel still ends normally.
+ */
+gemm_status gemm_test_preset_gate(gemm_tile_cfg tile_cfg, uint32_t held);
+
+/*
+ * Test helper: create a stream on `device` (current) whose kernels may only use
+ * the compute units set in `mask` (words x 32 bits, hipExtStreamCreateWithCUMask)
+ * and return it in *out_stream; release it with gemm_test_stream_destroy. This is
+ * the other reading of the worked example's concurrency cap (a CU mask; the plan's
+ * gate is the one the library uses, see max_concurrent): a mask must leave compute
+ * units on every XCD, since workgroups are sent to XCDs in turn. Errors:
+ * GEMM_E_INVALID_ARG (NULL, no unit named, a unit beyond the device's, more
+ * than 64 words), GEMM_E_DEVICE, GEMM_E_UNSUPPORTED (not gfx950), GEMM_E_HIP.
+ */
+gemm_status gemm_test_stream_cu_mask(void **out_stream, int32_t device, const uint32_t *mask, uint32_t words);
+
+/* Destroy a stream made by gemm_test_stream_cu_mask. */
+gemm_status gemm_test_stream_destroy(void *stream);
+
+/*
  * Occupy `n_wgs` compute units for `spin_ns` nanoseconds on `stream`: each
  * workgroup takes a whole CU's LDS, records {s_memrealtime at start, HW_ID,
  * XCC_ID, end} into d_log (4 uint64 per workgroup; may be NULL) and spins on the
@@ -289,8 +411,8 @@ gemm_status gemm_test_preset_counter(gemm_tile_cfg tile_cfg, uint32_t start);
  * only once all n_wgs workgroups have started, or GEMM_E_TIMEOUT after that
  * many milliseconds (the spoiler still ends on its own).
  */
-gemm_status gemm_spoiler_run(int32_t device, int32_t n_wgs, int64_t spin_ns, void *stream,
-                             uint64_t *d_log, double wait_resident_ms);
+gemm_status gemm_test_spoiler(int32_t device, int32_t n_wgs, int64_t spin_ns, void *stream,
+                              uint64_t *d_log, double wait_resident_ms);
 
 /*
  * Measurement helper (no page behind it; a fact about the part): run an

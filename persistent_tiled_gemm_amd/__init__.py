@@ -5,11 +5,12 @@ runs in the HIP library libptg_gemm.so built in this directory. There is no
 fallback; if the library is missing, loading it raises.
 
 The function names are the C ABI's: gemm_default_desc, gemm_create, gemm_run,
-gemm_run_grouped, gemm_read_log, gemm_plan_info_get, gemm_destroy,
+gemm_run_grouped, gemm_read_log, gemm_sync, gemm_plan_info_get, gemm_destroy,
 gemm_status_str, gemm_last_hip_error, gemm_test_preset_counter,
-gemm_spoiler_run, gemm_mfma_probe. Tensors are torch device tensors: A and B bf16 (or int16 /
-uint16 views of bf16 bits), C float32, all contiguous; streams are
-torch.cuda streams (default: the current stream).
+gemm_test_preset_gate, gemm_test_stream_cu_mask, gemm_test_stream_destroy,
+gemm_test_spoiler, gemm_mfma_probe. Tensors are torch device tensors: A and B
+bf16 (or int16 / uint16 views of bf16 bits), C float32, all contiguous; streams
+are torch.cuda streams (default: the current stream).
 """
 
 from __future__ import annotations
@@ -35,8 +36,9 @@ STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_E_INVALID_ARG", -2: "GEMM_E_SHAPE", -3: 
 
 # exported names, in the order of the header
 ABI_FUNCTIONS = ("gemm_default_desc", "gemm_create", "gemm_run", "gemm_run_grouped", "gemm_read_log",
-                 "gemm_plan_info_get", "gemm_destroy", "gemm_status_str", "gemm_last_hip_error",
-                 "gemm_test_preset_counter", "gemm_spoiler_run", "gemm_mfma_probe")
+                 "gemm_sync", "gemm_plan_info_get", "gemm_destroy", "gemm_status_str", "gemm_last_hip_error",
+                 "gemm_test_preset_counter", "gemm_test_preset_gate", "gemm_test_stream_cu_mask",
+                 "gemm_test_stream_destroy", "gemm_test_spoiler", "gemm_mfma_probe")
 
 
 class PtgError(RuntimeError):
@@ -52,7 +54,7 @@ class TileDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bm", "bn", "bk", "ring_depth", "claims_ahead", "claim_lead", "claim_policy", "raster", "raster_group", "static_workers",
         "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device", "tail_split", "group_order", "claim_group",
-        "b_layout")]
+        "b_layout", "gate_spin_limit", "k_rotation")]
 
 
 class TileRec(ctypes.Structure):
@@ -107,6 +109,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gemm_run_grouped.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                      P64, P64, P64, i32, vp, vp]
     lib.gemm_read_log.argtypes = [vp, ctypes.POINTER(TileRec), ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gemm_sync.argtypes = [vp]
     lib.gemm_plan_info_get.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.gemm_destroy.argtypes = [vp]
     lib.gemm_status_str.argtypes = [i32]
@@ -114,7 +117,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gemm_last_hip_error.argtypes = [vp]
     lib.gemm_last_hip_error.restype = ctypes.c_char_p
     lib.gemm_test_preset_counter.argtypes = [vp, u32]
-    lib.gemm_spoiler_run.argtypes = [i32, i32, i64, vp, vp, ctypes.c_double]
+    lib.gemm_test_preset_gate.argtypes = [vp, u32]
+    lib.gemm_test_stream_cu_mask.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(u32), u32]
+    lib.gemm_test_stream_destroy.argtypes = [vp]
+    lib.gemm_test_spoiler.argtypes = [i32, i32, i64, vp, vp, ctypes.c_double]
     lib.gemm_mfma_probe.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_double)]
     for name in ABI_FUNCTIONS:
@@ -275,10 +281,7 @@ def gemm_read_log(plan: Plan, cap: Optional[int] = None, strict: bool = True) ->
     st = load_library().gemm_read_log(plan.handle, buf, cap, ctypes.byref(n))
     if strict:
         _check(st, "gemm_read_log", plan)
-    arr = np.frombuffer(bytes(buf), dtype=TILE_REC_DTYPE, count=max(cap, 1))[: n.value].copy()
-    if not strict:
-        arr = arr  # status available through gemm_read_log_status
-    return arr
+    return np.frombuffer(bytes(buf), dtype=TILE_REC_DTYPE, count=max(cap, 1))[: n.value].copy()
 
 
 def gemm_read_log_status(plan: Plan, cap: Optional[int] = None):
@@ -292,6 +295,16 @@ def gemm_read_log_status(plan: Plan, cap: Optional[int] = None):
     return int(st), arr
 
 
+def gemm_sync(plan: Plan, strict: bool = True) -> int:
+    """gemm_sync: wait for the plan's last run and return (strict=False) or raise on (strict=True) the
+    device status of every run since the last check (a gate wait that ran out, a ring protocol
+    violation). Works with the tile log off."""
+    st = int(load_library().gemm_sync(plan.handle))
+    if strict:
+        _check(st, "gemm_sync", plan)
+    return st
+
+
 def gemm_plan_info_get(plan: Plan) -> dict:
     info = PlanInfo()
     _check(load_library().gemm_plan_info_get(plan.handle, ctypes.byref(info)), "gemm_plan_info_get", plan)
@@ -302,13 +315,50 @@ def gemm_test_preset_counter(plan: Plan, start: int) -> None:
     _check(load_library().gemm_test_preset_counter(plan.handle, int(start)), "gemm_test_preset_counter", plan)
 
 
-def gemm_spoiler_run(n_wgs: int, spin_ns: int, stream=None, log=None, wait_resident_ms: float = 0.0,
-                     device: int = 0) -> None:
-    """gemm_spoiler_run: occupy n_wgs CUs for spin_ns on `stream` (log: uint64 device tensor of 4*n_wgs)."""
+def gemm_test_preset_gate(plan: Plan, held: int) -> None:
+    _check(load_library().gemm_test_preset_gate(plan.handle, int(held)), "gemm_test_preset_gate", plan)
+
+
+class CuMaskStream:
+    """A stream restricted to the compute units of a mask (gemm_test_stream_cu_mask). `torch_stream` is
+    the same stream as a torch.cuda.ExternalStream, for events and for the binding's stream arguments."""
+
+    def __init__(self, mask_words: Sequence[int], device: int = 0):
+        import torch
+        words = [int(w) & 0xFFFFFFFF for w in mask_words]
+        arr = (ctypes.c_uint32 * len(words))(*words)
+        h = ctypes.c_void_p()
+        _check(load_library().gemm_test_stream_cu_mask(ctypes.byref(h), int(device), arr, len(words)),
+               "gemm_test_stream_cu_mask")
+        self._handle = h
+        self.torch_stream = torch.cuda.ExternalStream(h.value, device=torch.device("cuda", int(device)))
+
+    @property
+    def cuda_stream(self) -> int:
+        return int(self._handle.value or 0)
+
+    def destroy(self) -> None:
+        if self._handle:
+            self.torch_stream.synchronize()
+            _check(load_library().gemm_test_stream_destroy(self._handle), "gemm_test_stream_destroy")
+            self._handle = ctypes.c_void_p()
+
+
+def gemm_test_stream_cu_mask(mask_words: Sequence[int], device: int = 0) -> CuMaskStream:
+    return CuMaskStream(mask_words, device)
+
+
+def gemm_test_stream_destroy(stream: CuMaskStream) -> None:
+    stream.destroy()
+
+
+def gemm_test_spoiler(n_wgs: int, spin_ns: int, stream=None, log=None, wait_resident_ms: float = 0.0,
+                      device: int = 0) -> None:
+    """gemm_test_spoiler: occupy n_wgs CUs for spin_ns on `stream` (log: uint64 device tensor of 4*n_wgs)."""
     log_ptr = ctypes.c_void_p(log.data_ptr()) if log is not None else ctypes.c_void_p()
-    st = load_library().gemm_spoiler_run(int(device), int(n_wgs), int(spin_ns), ctypes.c_void_p(_stream_ptr(stream)),
-                                         log_ptr, float(wait_resident_ms))
-    _check(st, "gemm_spoiler_run")
+    st = load_library().gemm_test_spoiler(int(device), int(n_wgs), int(spin_ns), ctypes.c_void_p(_stream_ptr(stream)),
+                                          log_ptr, float(wait_resident_ms))
+    _check(st, "gemm_test_spoiler")
 
 
 def gemm_mfma_probe(iters: int = 20000, random_operands: bool = True, mfma_block: int = 16, device: int = 0) -> dict:
@@ -340,7 +390,7 @@ def matmul(A, B, mode="dynamic", plan: Optional[Plan] = None, stream=None):
     try:
         gemm_run(A, B, C, plan, mode=mode, stream=stream)
         if own:
-            torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+            gemm_sync(plan)  # waits for the run and raises on a device-side failure
     finally:
         if own:
             plan.destroy()

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/ptg_gemm.h: plan creation and
 // validation, launch sizing per scheduler, per-run scratch reset, tile-log
-// readback, the spoiler and failure-forcing helpers.
+// and device-status readback, the spoiler, CU-masked streams and the
+// failure-forcing helpers.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -30,8 +31,10 @@ struct gemm_plan {
   int lds_bytes = 0;
   int dyn_lds = 0;
   // device scratch: two sets of [SchedCtrl][arrivals u32 x kMaxSplitTiles][visits u32 x
-  // log_capacity], plus the log and (tail splitting on) the partial-sum workspace
+  // log_capacity] followed by the sticky status word, plus the log and (tail
+  // splitting on) the partial-sum workspace
   unsigned char *d_ctrl_block = nullptr;
+  uint32_t *d_status = nullptr;  // error bits of every run since the host last read them
   float *d_ws = nullptr;
   int64_t ws_tiles = 0;  // BM x BN fp32 partial slots in d_ws
   size_t ctrl_set_bytes = 0;
@@ -44,6 +47,9 @@ struct gemm_plan {
   std::vector<KernelProblem> last_groups;  // what d_groups holds
   uint32_t preset = 0;
   bool preset_pending = false;
+  uint32_t gate_preset = 0;
+  bool gate_preset_pending = false;
+  hipEvent_t stream_switch = nullptr;  // orders a run on a new stream after the plan's last stream
   // last run
   hipStream_t last_stream = nullptr;
   bool has_run = false;
@@ -96,9 +102,47 @@ gemm_status check_current_device(gemm_plan *p) {
   return GEMM_OK;
 }
 
+// A plan's scratch (scheduler state, grouped table, split workspace) is used by
+// one run at a time. Runs on one stream are ordered by the stream; a run on a
+// different stream than the last one first waits (on the device) for
+// everything enqueued on the last stream so far. No host synchronisation.
+gemm_status order_after_last_stream(gemm_plan *p, hipStream_t s) {
+  if (!p->has_run || s == p->last_stream) return GEMM_OK;
+  hipError_t e = hipEventRecord(p->stream_switch, p->last_stream);
+  if (e != hipSuccess) return hip_fail(p, e, "hipEventRecord(stream switch)");
+  e = hipStreamWaitEvent(s, p->stream_switch, 0);
+  if (e != hipSuccess) return hip_fail(p, e, "hipStreamWaitEvent(stream switch)");
+  return GEMM_OK;
+}
+
+// Synchronise the last run's stream, read the sticky device status and clear it.
+gemm_status take_device_status(gemm_plan *p) {
+  if (!p->has_run) return GEMM_OK;
+  hipError_t e = hipStreamSynchronize(p->last_stream);
+  if (e != hipSuccess) return hip_fail(p, e, "hipStreamSynchronize");
+  uint32_t st = 0;
+  e = hipMemcpy(&st, p->d_status, sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(status)");
+  if (st == 0) return GEMM_OK;
+  const uint32_t zero = 0;
+  e = hipMemcpy(p->d_status, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(status clear)");
+  p->last_error = "device-side scheduler error flags " + std::to_string(st) +
+                  ((st & 1u) ? " (a workgroup gave up waiting at the concurrency gate and computed nothing)" : "") +
+                  ((st & 2u) ? " (a claim-ring record answered the wrong ordinal)" : "");
+  return (st & 2u) ? GEMM_E_SCHED : GEMM_E_TIMEOUT;
+}
+
 unsigned char *ctrl_set(gemm_plan *p, uint64_t run) { return p->d_ctrl_block + (run & 1u) * p->ctrl_set_bytes; }
 constexpr size_t kArrivalsOffset = sizeof(SchedCtrl);
 constexpr size_t kVisitsOffset = sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)ptg::kMaxSplitTiles;
+
+// K order of the default plan (see gemm_tile_desc.k_rotation).
+constexpr int32_t kDefaultKRotation = 0;
+
+// Polls of the concurrency gate before a workgroup gives up (each well under a
+// microsecond: a few seconds at most).
+constexpr uint32_t kDefaultGateSpinLimit = 1u << 22;
 
 // Fewest k-steps (of bk = 32) a K-chunk of a split tile gets.
 constexpr int64_t kMinChunkSteps = 8;
@@ -155,12 +199,20 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   args.claim_lead = p->desc.claim_lead;
   args.claim_policy = p->desc.claim_policy;
   args.raster_group = p->desc.raster == 1 ? p->desc.raster_group : 1;
+  args.k_rotation = p->desc.k_rotation;
   args.counter_base = 0;
   if (mode == GEMM_SCHED_DYNAMIC && p->preset_pending) {
     args.counter_base = p->preset;
     p->preset_pending = false;
   }
   args.max_concurrent = p->desc.max_concurrent;
+  args.gate_spin_limit = p->desc.gate_spin_limit > 0 ? (uint32_t)p->desc.gate_spin_limit : kDefaultGateSpinLimit;
+  args.gate_base = 0;
+  if (p->gate_preset_pending) {
+    args.gate_base = p->gate_preset;
+    p->gate_preset_pending = false;
+  }
+  args.status = p->d_status;
   args.log_cap = p->desc.log_capacity;
   unsigned char *cur = ctrl_set(p, p->runs), *nxt = ctrl_set(p, p->runs + 1);
   args.ctrl = reinterpret_cast<SchedCtrl *>(cur);
@@ -227,6 +279,8 @@ gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t de
   out->group_order = 0;
   out->claim_group = 1;
   out->b_layout = 0;
+  out->gate_spin_limit = 0;
+  out->k_rotation = kDefaultKRotation;
   return GEMM_OK;
 }
 
@@ -242,7 +296,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
       d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT || d.group_order < 0 ||
       d.group_order > 1 || d.claim_group < 0 || d.claim_group > GEMM_MAX_CLAIM_GROUP || d.b_layout < 0 ||
-      d.b_layout > 1)
+      d.b_layout > 1 || d.gate_spin_limit < 0 || d.k_rotation < 0 || d.k_rotation > 2)
     return GEMM_E_INVALID_ARG;
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -282,11 +336,12 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   p->static_workers = d.static_workers > 0 ? d.static_workers : occ * p->cu_count;
 
   p->ctrl_set_bytes = (kVisitsOffset + sizeof(uint32_t) * (size_t)std::max(d.log_capacity, 1) + 255) & ~(size_t)255;
-  if (hipMalloc(&p->d_ctrl_block, 2 * p->ctrl_set_bytes) != hipSuccess) {
+  if (hipMalloc(&p->d_ctrl_block, 2 * p->ctrl_set_bytes + 256) != hipSuccess) {
     delete p;
     return GEMM_E_NOMEM;
   }
-  if (hipMemset(p->d_ctrl_block, 0, 2 * p->ctrl_set_bytes) != hipSuccess) {
+  p->d_status = reinterpret_cast<uint32_t *>(p->d_ctrl_block + 2 * p->ctrl_set_bytes);
+  if (hipMemset(p->d_ctrl_block, 0, 2 * p->ctrl_set_bytes + 256) != hipSuccess) {
     gemm_destroy(p);
     return GEMM_E_HIP;
   }
@@ -321,6 +376,11 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
     gemm_destroy(p);
     return GEMM_E_HIP;
   }
+  if (hipEventCreateWithFlags(&p->stream_switch, hipEventDisableTiming) != hipSuccess) {
+    p->stream_switch = nullptr;
+    gemm_destroy(p);
+    return GEMM_E_HIP;
+  }
   *out = p;
   return GEMM_OK;
 }
@@ -352,6 +412,8 @@ gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t 
   args.single.unit_start = 0;
   args.groups = nullptr;
   args.G = 1;
+  st = order_after_last_stream(p, static_cast<hipStream_t>(stream));
+  if (st != GEMM_OK) return st;
   p->last_tile_start.assign(1, 0);
   p->last_k.assign(1, (int32_t)K);
   p->last_unit_map.clear();
@@ -419,6 +481,8 @@ gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const 
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  st = order_after_last_stream(p, s);
+  if (st != GEMM_OK) return st;
   const bool same = p->last_groups.size() == table.size() &&
                     std::memcmp(p->last_groups.data(), table.data(), sizeof(KernelProblem) * table.size()) == 0;
   if (!same) {
@@ -452,14 +516,17 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
   gemm_plan *p = tile_cfg;
   if (!p || !n_out || (cap > 0 && !host_out)) return GEMM_E_INVALID_ARG;
   *n_out = 0;
-  if (!p->has_run || p->desc.log_capacity == 0) return GEMM_OK;
-  hipError_t e = hipStreamSynchronize(p->last_stream);
-  if (e != hipSuccess) return hip_fail(p, e, "hipStreamSynchronize");
+  if (!p->has_run) return GEMM_OK;
+  // the device status first (it also synchronises the stream): it is reported
+  // whether or not the log is on
+  const gemm_status dev_status = take_device_status(p);
+  if (dev_status == GEMM_E_HIP) return dev_status;
+  if (p->desc.log_capacity == 0) return dev_status;
+  hipError_t e = hipSuccess;
   const size_t n = (size_t)std::min<int64_t>(p->last_items, p->desc.log_capacity);
   const size_t m = std::min(n, cap);
   std::vector<TileRecDev> recs(m);
   std::vector<uint32_t> visits(m);
-  SchedCtrl ctrl;
   if (m > 0) {
     e = hipMemcpy(recs.data(), p->d_log, sizeof(TileRecDev) * m, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(log)");
@@ -467,8 +534,6 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
                   hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(visits)");
   }
-  e = hipMemcpy(&ctrl, ctrl_set(p, p->runs - 1), sizeof(ctrl), hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(ctrl)");
   const int64_t bk = p->desc.bk;
   for (size_t i = 0; i < m; ++i) {
     gemm_tile_rec &r = host_out[i];
@@ -515,11 +580,13 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
     r.r1 = recs[i].r1;
   }
   *n_out = m;
-  if (ctrl.error != 0) {
-    p->last_error = "device-side scheduler error flags " + std::to_string(ctrl.error);
-    return (ctrl.error & 2u) ? GEMM_E_SCHED : GEMM_E_TIMEOUT;
-  }
-  return GEMM_OK;
+  return dev_status;
+}
+
+gemm_status gemm_sync(gemm_tile_cfg tile_cfg) {
+  gemm_plan *p = tile_cfg;
+  if (!p) return GEMM_E_INVALID_ARG;
+  return take_device_status(p);
 }
 
 gemm_status gemm_plan_info_get(gemm_tile_cfg tile_cfg, gemm_plan_info *out) {
@@ -554,6 +621,7 @@ gemm_status gemm_destroy(gemm_tile_cfg tile_cfg) {
   if (p->d_groups) (void)hipFree(p->d_groups);
   if (p->h_groups) (void)hipHostFree(p->h_groups);
   if (p->groups_uploaded) (void)hipEventDestroy(p->groups_uploaded);
+  if (p->stream_switch) (void)hipEventDestroy(p->stream_switch);
   delete p;
   return GEMM_OK;
 }
@@ -571,8 +639,46 @@ gemm_status gemm_test_preset_counter(gemm_tile_cfg tile_cfg, uint32_t start) {
   return GEMM_OK;
 }
 
-gemm_status gemm_spoiler_run(int32_t device, int32_t n_wgs, int64_t spin_ns, void *stream, uint64_t *d_log,
-                             double wait_resident_ms) {
+gemm_status gemm_test_preset_gate(gemm_tile_cfg tile_cfg, uint32_t held) {
+  gemm_plan *p = tile_cfg;
+  if (!p) return GEMM_E_INVALID_ARG;
+  p->gate_preset = held;
+  p->gate_preset_pending = true;
+  return GEMM_OK;
+}
+
+gemm_status gemm_test_stream_cu_mask(void **out_stream, int32_t device, const uint32_t *mask, uint32_t words) {
+  if (!out_stream || !mask || words == 0 || words > 64) return GEMM_E_INVALID_ARG;
+  *out_stream = nullptr;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GEMM_E_HIP;
+  if (cur != device) return GEMM_E_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return GEMM_E_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_E_UNSUPPORTED;
+  // every compute unit the mask names must exist, and at least one must be named
+  uint32_t named = 0;
+  for (uint32_t w = 0; w < words; ++w) {
+    for (uint32_t b = 0; b < 32; ++b) {
+      if (!((mask[w] >> b) & 1u)) continue;
+      if ((int64_t)w * 32 + b >= prop.multiProcessorCount) return GEMM_E_INVALID_ARG;
+      ++named;
+    }
+  }
+  if (named == 0) return GEMM_E_INVALID_ARG;
+  hipStream_t s = nullptr;
+  if (hipExtStreamCreateWithCUMask(&s, words, mask) != hipSuccess) return GEMM_E_HIP;
+  *out_stream = s;
+  return GEMM_OK;
+}
+
+gemm_status gemm_test_stream_destroy(void *stream) {
+  if (!stream) return GEMM_E_INVALID_ARG;
+  return hipStreamDestroy(static_cast<hipStream_t>(stream)) == hipSuccess ? GEMM_OK : GEMM_E_HIP;
+}
+
+gemm_status gemm_test_spoiler(int32_t device, int32_t n_wgs, int64_t spin_ns, void *stream, uint64_t *d_log,
+                              double wait_resident_ms) {
   if (n_wgs <= 0 || spin_ns < 0 || spin_ns > 60ll * 1000 * 1000 * 1000) return GEMM_E_INVALID_ARG;
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return GEMM_E_HIP;

@@ -113,7 +113,14 @@ struct RingRec {
 };
 
 static constexpr int kRingDepth = 3;  // LDS slots; a run uses args.ring_depth (2 or 3) of them
-static constexpr uint32_t kGateSpinLimit = 1u << 22;  // polls of well under 1 us: a few seconds at most
+
+// Record a device-side failure: in this run's control block (bit set of the
+// run) and in the plan's status word, which only the host clears, so a failure
+// of any run stays visible until the host has read it.
+__device__ __forceinline__ void flag_error(const KernelArgs &a, uint32_t bit) {
+  __hip_atomic_fetch_or(&a.ctrl->error, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_or(a.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Ask the scheduler for an alternation of one MFMA and one LDS read in the
 // current scheduling region (then the remaining MFMAs or reads).
@@ -264,10 +271,12 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
   // ---- optional concurrency gate: at most max_concurrent workgroups compute at once
   if (args.max_concurrent > 0) {
     if (tid == 0) {
+      // a bounded wait: at most gate_spin_limit polls (the host may preset
+      // gate_base slots as taken, so that every wait runs out: failure forcing)
       uint32_t ok = 0;
-      for (uint32_t it = 0; it < kGateSpinLimit; ++it) {
+      for (uint32_t it = 0; it < args.gate_spin_limit; ++it) {
         uint32_t cur = __hip_atomic_load(&args.ctrl->gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (cur < (uint32_t)args.max_concurrent &&
+        if (cur + args.gate_base < (uint32_t)args.max_concurrent &&
             __hip_atomic_compare_exchange_strong(&args.ctrl->gate, &cur, cur + 1u, __ATOMIC_ACQUIRE,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
           ok = 1;
@@ -275,7 +284,9 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         }
         __builtin_amdgcn_s_sleep(4);
       }
-      if (!ok) __hip_atomic_fetch_or(&args.ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // a workgroup that gives up computes nothing: its units are lost in the
+      // static and non-persistent modes, so the failure is recorded for the host
+      if (!ok) flag_error(args, 1u);
       gate_ok = ok;
     }
     __syncthreads();
@@ -427,6 +438,31 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // k-steps [kb, ke) of this unit: all of them, or an even share for a K-chunk
     const int32_t kb = split ? (int32_t)((uint32_t)nk * chunk / (uint32_t)args.split_chunks) : 0;
     const int32_t ke = split ? (int32_t)((uint32_t)nk * (chunk + 1u) / (uint32_t)args.split_chunks) : nk;
+    // K order of the unit: logical k-step kt (kb <= kt < ke) reads physical k-step
+    // kb + ((kt - kb + rot) mod (ke - kb)). When every workgroup walks K from the
+    // same end, all concurrent operand reads of the machine share their low
+    // address bits (the same 64-byte column of every row of A): measured on a
+    // streaming probe of that pattern, 4.5 TB/s against 5.9 TB/s when each CU
+    // starts at a different column. A rotation spreads them. It changes only the
+    // order of the fp32 sum inside a tile (a function of the unit id alone, so
+    // every scheduler still gives bitwise the same C). Off when K has a partial
+    // k-step (the K-tail masking assumes that step comes last).
+    const int32_t nsteps = ke - kb;
+    int32_t rot = 0;
+    if (args.k_rotation != 0 && nsteps > 1 && K % CF::BK == 0) {
+      if (args.k_rotation == 1) {
+        // one phase per XCD region (unit id mod 8): the workgroups of one XCD,
+        // which share operand panels through its L2, keep walking K together
+        rot = (int32_t)((item % (uint32_t)kXcdRegions) * (uint32_t)nsteps / (uint32_t)kXcdRegions);
+      } else {
+        // a phase per unit (multiplicative hash of the item id)
+        rot = (int32_t)(((item * 2654435761u) >> 16) % (uint32_t)nsteps);
+      }
+      rot = (int32_t)wave_uniform((uint32_t)rot);
+    }
+    // physical k-step of logical k-step kt (logical steps past ke read zeros
+    // through a dead resource, whatever their base)
+    auto phys = [&](int32_t kt) -> int32_t { return kt + rot >= ke ? kt + rot - nsteps : kt + rot; };
 
     // voffset of load j of a k-step with no partial K: chunks outside the matrix
     // (row / column edges) read as zero via kBufOob. The A swizzle of load j's
@@ -475,8 +511,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     };
     // all loads of k-step kt into stage dst, back to back (prologue)
     auto issue_all = [&](int st, int32_t kt) {
-      const i32x4 ra = make_rsrc_words(a_tile + kt * CF::BK, kt < ke);
-      const i32x4 rb = make_rsrc_words(b_kstep(kt), kt < ke);
+      const i32x4 ra = make_rsrc_words(a_tile + phys(kt) * CF::BK, kt < ke);
+      const i32x4 rb = make_rsrc_words(b_kstep(phys(kt)), kt < ke);
       const uint32_t base = lds_addr(smem);
 #pragma unroll
       for (int j = 0; j < CF::A_LOADS + CF::B_LOADS; ++j)
@@ -532,8 +568,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       i32x4 ra = {0, 0, 0, 0}, rb = {0, 0, 0, 0};
       const uint32_t lbase = lds_addr(smem);
       if (count > 0) {
-        ra = make_rsrc_words(a_tile + kt_load * CF::BK, kt_load < ke);
-        rb = make_rsrc_words(b_kstep(kt_load), kt_load < ke);
+        ra = make_rsrc_words(a_tile + phys(kt_load) * CF::BK, kt_load < ke);
+        rb = make_rsrc_words(b_kstep(phys(kt_load)), kt_load < ke);
       }
       i16x4 lo[CF::NI];
 #pragma unroll
@@ -693,8 +729,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
           const unsigned char *sa = smem + CF::a_off(rst);
           const unsigned char *sb = smem + CF::b_off(rst);
           const int32_t kt_load = kt + 4;
-          const i32x4 ra = make_rsrc_words(a_tile + kt_load * CF::BK, kt_load < ke);
-          const i32x4 rb = make_rsrc_words(b_kstep(kt_load), kt_load < ke);
+          const i32x4 ra = make_rsrc_words(a_tile + phys(kt_load) * CF::BK, kt_load < ke);
+          const i32x4 rb = make_rsrc_words(b_kstep(phys(kt_load)), kt_load < ke);
           const uint32_t lbase = lds_addr(smem);
           i16x4 lo[CF::NI];
 #pragma unroll
@@ -947,7 +983,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       unit = wave_uniform(rec.tile);
       if (seq != ord + 1) {
         // the ring protocol was violated: stop this worker and flag it
-        if (tid == 0) __hip_atomic_fetch_or(&args.ctrl->error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) flag_error(args, 2u);
         valid = false;
       }
     } else if constexpr (MODE == kStatic) {

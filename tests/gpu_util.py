@@ -103,3 +103,41 @@ def check_log(plan, mode, T, P=None, expected_tiles=None, K=None, tiles=None, gr
         errs = check_k_cover(ran["tile"], ran["k_begin"], ran["k_end"], T if tiles is None else tiles, K)
         assert not errs, errs
     return log
+
+
+def sample_rows(M, tile, rng, per_tile_row=1):
+    """Rows to compare with the oracle: per_tile_row random rows of every tile row, plus the first and last."""
+    rows = []
+    for t in range(-(-M // tile)):
+        lo, hi = t * tile, min(M, (t + 1) * tile)
+        rows += rng.integers(lo, hi, size=per_tile_row).tolist()
+    rows += [0, M - 1]
+    return np.array(sorted(set(rows)))
+
+
+class GroupedReference:
+    """Oracle rows for every problem of a grouped run, computed once and checked
+    against any number of runs: every C_g is NaN-free as a whole, and its sampled
+    rows (every tile row of every problem) meet the acceptance bound."""
+
+    def __init__(self, problems, seed, tile=256, per_tile_row=1):
+        rng = np.random.default_rng(seed)
+        self.problems = problems
+        self.rows = [sample_rows(q.M, tile, rng, per_tile_row) for q in problems]
+        self.refs = [gemm_ref_rows(q.a_bits, q.b_bits, r) for q, r in zip(problems, self.rows)]
+        self.amax = [maxabs(q.a_bits) for q in problems]
+        self.bmax = [maxabs(q.b_bits) for q in problems]
+
+    def check(self, Cs, what=""):
+        """Cs: the run's C_g, as device tensors or host arrays, in problem order."""
+        torch = torch_mod()
+        assert len(Cs) == len(self.problems)
+        for g, (q, C) in enumerate(zip(self.problems, Cs)):
+            if isinstance(C, np.ndarray):
+                assert not np.isnan(C).any(), (what, g)
+                got = C[self.rows[g]]
+            else:
+                assert not torch.isnan(C).any().item(), (what, g)
+                got = C[torch.as_tensor(self.rows[g], device=C.device)].cpu().numpy()
+            rep = check_result(got, self.refs[g], q.K, self.amax[g], self.bmax[g])
+            assert rep["ok"], (what, g, rep)

@@ -50,6 +50,7 @@ def test_status_strings_and_defaults(lib):
     assert ptg.gemm_status_str(-99) == "unknown status"
     d = ptg.gemm_default_desc(256, 0)
     assert (d.bm, d.bn, d.bk, d.ring_depth, d.claims_ahead, d.claim_lead, d.claim_policy) == (256, 256, 32, 3, 1, 4, 1)
+    assert (d.log_capacity, d.max_concurrent, d.gate_spin_limit, d.tail_split, d.claim_group) == (0, 0, 0, 0, 1)
     d = ptg.gemm_default_desc(128, 0)
     assert (d.bm, d.bn) == (128, 128)
     with pytest.raises(ptg.PtgError):
@@ -65,8 +66,12 @@ def test_null_arguments_are_rejected_before_any_hip_call(lib):
     assert lib.gemm_plan_info_get(None, None) == -1
     assert lib.gemm_destroy(None) == 0
     assert lib.gemm_test_preset_counter(None, 3) == -1
+    assert lib.gemm_test_preset_gate(None, 3) == -1
+    assert lib.gemm_sync(None) == -1
+    assert lib.gemm_test_stream_destroy(None) == -1
+    assert lib.gemm_test_stream_cu_mask(None, 0, None, 0) == -1
     assert lib.gemm_last_hip_error(None) == b""
-    assert lib.gemm_spoiler_run(0, 0, 1000, None, None, 0.0) == -1
+    assert lib.gemm_test_spoiler(0, 0, 1000, None, None, 0.0) == -1
     assert lib.gemm_mfma_probe(0, 100, 1, 16, None, None) == -1
 
 

@@ -12,7 +12,7 @@ import pytest
 
 import persistent_tiled_gemm_amd as ptg
 from oracle.sched_model import lpt_claim_order
-from tests.gpu_util import assert_close_full, assert_close_rows, check_log, make_plan, say, torch_mod
+from tests.gpu_util import GroupedReference, assert_close_full, check_log, make_plan, say, torch_mod
 from workloads import make_problem, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -62,7 +62,7 @@ def test_lpt_order_grouped_uneven_workload():
     w = make_workload("grouped_uneven")
     plan = ptg.gemm_create(tile_edge=256, log_capacity=1024, group_order=1)
     want = lpt_claim_order([q.K for q in w.problems], [16] * 64)
-    rng = np.random.default_rng(9)
+    ref = GroupedReference(w.problems, seed=9)
     for mode in MODES:
         say(f"case lpt grouped_uneven mode={mode}")
         cs = _run_grouped(w.problems, plan, mode)
@@ -70,9 +70,7 @@ def test_lpt_order_grouped_uneven_workload():
         log = check_log(plan, mode, 1024, P=info["last_grid"] if mode == "static" else None,
                         K=_tile_k(w.problems, 256))
         assert log["tile"].tolist() == want
-        for g in range(0, 64, 9):
-            rows = sorted(set(rng.integers(0, 1024, size=6).tolist() + [0, 1023]))
-            assert_close_rows(w.problems[g], cs[g], rows)
+        ref.check(cs, f"lpt {mode}")      # all 64 problems
     plan.destroy()
 
 
@@ -98,7 +96,7 @@ def test_lpt_dealt_to_contiguous_regions():
     # regions' K sums differ by at most max K - min K
     sums = [sum(ks[want[r * 128 + 16 * j] // 16] for j in range(8)) for r in range(8)]
     assert max(sums) - min(sums) <= max(ks) - min(ks)
-    rng = np.random.default_rng(11)
+    ref = GroupedReference(w.problems, seed=11)
     for mode in MODES:
         say(f"case lpt dealt grouped_uneven policy=2 mode={mode}")
         cs = _run_grouped(w.problems, plan, mode)
@@ -106,9 +104,7 @@ def test_lpt_dealt_to_contiguous_regions():
         log = check_log(plan, mode, 1024, P=info["last_grid"] if mode == "static" else None,
                         K=_tile_k(w.problems, 256))
         assert log["tile"].tolist() == want
-        for g in range(3, 64, 10):
-            rows = sorted(set(rng.integers(0, 1024, size=6).tolist() + [0, 1023]))
-            assert_close_rows(w.problems[g], cs[g], rows)
+        ref.check(cs, f"lpt dealt {mode}")   # all 64 problems
     plan.destroy()
 
 
