@@ -314,6 +314,31 @@ gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t 
                      int32_t sched_mode, gemm_tile_cfg tile_cfg, void *stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The same product as
+ * gemm_run with the plan gemm_default_desc(256) gives (256 x 256 tiles,
+ * per-XCD claim counters, one claim ahead, log off, no split tail, no claim
+ * groups, no concurrency gate, B as K x N), with no plan: the scheduler state
+ * lives in a library-owned device array of 768 bytes per device (two control
+ * sets and a status word), which each device keeps until the process ends. Its
+ * size does not depend on M, N or K; sizes beyond the library limits are
+ * refused (GEMM_E_SHAPE) as by gemm_run. The first call on a device enqueues,
+ * before the GEMM, a small kernel that clears the array. Calls never allocate,
+ * free or synchronise.
+ * All calls on one device share that array, and each call leaves the next
+ * call's control set cleared: calls on one device must not overlap (enqueue
+ * them on one stream, or order them); overlapping calls race on the claim
+ * counters. d_status (optional, 4-byte aligned device pointer, caller-owned
+ * and caller-cleared) receives the error bits a plan's gemm_sync would report
+ * (bit 1: a claim-ring record for the wrong ordinal; the gate bit cannot occur
+ * without a gate); with NULL they go to the array's own status word, which no
+ * call reports. Errors: as gemm_run, plus GEMM_E_UNSUPPORTED (current device
+ * not gfx950) and GEMM_E_INVALID_ARG (misaligned d_status).
+ */
+gemm_status gemm_run_noalloc(const void *A, const void *B, float *C, int64_t M, int64_t N, int64_t K,
+                             int32_t sched_mode, uint32_t *d_status, void *stream);
+
+/*
  * Grouped variant: G independent problems C_g = A_g.B_g in one launch, their
  * tiles numbered problem after problem: the uneven-cost work the "B200 Cluster
  * Persistent Scheduler" page sends to the dynamic scheduler (section "E -

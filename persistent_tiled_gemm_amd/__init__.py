@@ -5,7 +5,7 @@ runs in the HIP library libptg_gemm.so built in this directory. There is no
 fallback; if the library is missing, loading it raises.
 
 The function names are the C ABI's: gemm_default_desc, gemm_create, gemm_run,
-gemm_run_grouped, gemm_read_log, gemm_sync, gemm_plan_info_get, gemm_destroy,
+gemm_run_noalloc, gemm_run_grouped, gemm_read_log, gemm_sync, gemm_plan_info_get, gemm_destroy,
 gemm_status_str, gemm_last_hip_error, gemm_test_preset_counter,
 gemm_test_preset_gate, gemm_test_stream_cu_mask, gemm_test_stream_destroy,
 gemm_test_spoiler, gemm_mfma_probe. Tensors are torch device tensors: A and B
@@ -35,7 +35,7 @@ STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_E_INVALID_ARG", -2: "GEMM_E_SHAPE", -3: 
                 -8: "GEMM_E_SCHED"}
 
 # exported names, in the order of the header
-ABI_FUNCTIONS = ("gemm_default_desc", "gemm_create", "gemm_run", "gemm_run_grouped", "gemm_read_log",
+ABI_FUNCTIONS = ("gemm_default_desc", "gemm_create", "gemm_run", "gemm_run_noalloc", "gemm_run_grouped", "gemm_read_log",
                  "gemm_sync", "gemm_plan_info_get", "gemm_destroy", "gemm_status_str", "gemm_last_hip_error",
                  "gemm_test_preset_counter", "gemm_test_preset_gate", "gemm_test_stream_cu_mask",
                  "gemm_test_stream_destroy", "gemm_test_spoiler", "gemm_mfma_probe")
@@ -106,6 +106,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gemm_default_desc.argtypes = [ctypes.POINTER(TileDesc), i32, i32]
     lib.gemm_create.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(TileDesc)]
     lib.gemm_run.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, vp]
+    lib.gemm_run_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, vp]
     lib.gemm_run_grouped.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                      P64, P64, P64, i32, vp, vp]
     lib.gemm_read_log.argtypes = [vp, ctypes.POINTER(TileRec), ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
@@ -250,6 +251,18 @@ def gemm_run_raw(A_ptr: int, B_ptr: int, C_ptr: int, M: int, N: int, K: int, pla
                                        int(M), int(N), int(K), _mode(mode),
                                        plan.handle if plan is not None else None,
                                        ctypes.c_void_p(_stream_ptr(stream))))
+
+
+def gemm_run_noalloc(A, B, C, mode="dynamic", status=None, stream=None) -> None:
+    """gemm_run_noalloc: C = A.B with the default 256 x 256 configuration and no plan; the library
+    allocates nothing (its scheduler state is a fixed device array). status: optional int32/uint32
+    device tensor of one element that receives device error bits."""
+    M, N, K = _check_operands(A, B, C, 0)
+    sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p()
+    st = load_library().gemm_run_noalloc(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
+                                         ctypes.c_void_p(C.data_ptr()), M, N, K, _mode(mode), sp,
+                                         ctypes.c_void_p(_stream_ptr(stream)))
+    _check(st, "gemm_run_noalloc")
 
 
 def gemm_run_grouped(As: Sequence, Bs: Sequence, Cs: Sequence, plan: Plan, mode="dynamic", stream=None) -> None:

@@ -9,6 +9,7 @@
 #include <climits>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <thread>
@@ -238,6 +239,61 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   return GEMM_OK;
 }
 
+// ---- scratch of gemm_run_noalloc: the scheduler state in a file-scope device
+// array (each device holds its own copy until the process ends), so the entry
+// point never allocates. Layout: two 256-byte control sets (run i uses set
+// i % 2 and clears the other for run i + 1, as a plan's sets do), then a
+// 256-byte status word block. The configuration is fixed (no log, no split
+// tail, no gate), so nothing in it grows with the problem.
+constexpr size_t kNoallocSetBytes = 256;
+constexpr size_t kNoallocScratchBytes = 2 * kNoallocSetBytes + 256;
+static_assert(sizeof(SchedCtrl) <= kNoallocSetBytes, "control set");
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+__global__ void ptg_zero_words(uint32_t *p, uint32_t n) {
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+struct NoallocDevice {
+  bool ready = false;
+  unsigned char *ptr = nullptr;  // device address of `scratch` on this device
+  int cu_count = 0;
+  int occupancy = 0;
+  uint64_t runs = 0;
+};
+constexpr int kNoallocMaxDevices = 64;
+NoallocDevice g_noalloc[kNoallocMaxDevices];
+std::mutex g_noalloc_mutex;
+
+// Once per device, with that device current: check it, resolve the device
+// address of `scratch` (the array's name is only a host-side stand-in) and
+// clear the array with a fill kernel on `s` (not a memset, so a caller that
+// captures the first call into a graph records a kernel node).
+gemm_status noalloc_setup(int dev, hipStream_t s, NoallocDevice **out) {
+  NoallocDevice &d = g_noalloc[dev];
+  if (d.ready) {
+    *out = &d;
+    return GEMM_OK;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_E_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_E_UNSUPPORTED;
+  void *ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return GEMM_E_HIP;
+  int occ = 0;
+  if (ptg::gemm_occupancy(256, 0, &occ) != hipSuccess || occ < 1) return GEMM_E_HIP;
+  hipLaunchKernelGGL(ptg_zero_words, dim3(1), dim3(64), 0, s, static_cast<uint32_t *>(ptr),
+                     (uint32_t)(kNoallocScratchBytes / sizeof(uint32_t)));
+  if (hipGetLastError() != hipSuccess) return GEMM_E_HIP;
+  d.ptr = static_cast<unsigned char *>(ptr);
+  d.cu_count = prop.multiProcessorCount;
+  d.occupancy = occ;
+  d.runs = 0;
+  d.ready = true;
+  *out = &d;
+  return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -418,6 +474,68 @@ gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t 
   p->last_k.assign(1, (int32_t)K);
   p->last_unit_map.clear();
   return launch(p, sched_mode, false, args, tiles, K, static_cast<hipStream_t>(stream));
+}
+
+gemm_status gemm_run_noalloc(const void *A, const void *B, float *C, int64_t M, int64_t N, int64_t K,
+                             int32_t sched_mode, uint32_t *d_status, void *stream) {
+  if (sched_mode < GEMM_SCHED_NONPERSISTENT || sched_mode > GEMM_SCHED_DYNAMIC) return GEMM_E_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_status) & 3u) != 0) return GEMM_E_INVALID_ARG;
+  gemm_status st = check_problem(A, B, C, M, N, K);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  const int64_t tm = ceil_div(M, 256), tn = ceil_div(N, 256);
+  const int64_t tiles = tm * tn;
+  if (tiles > GEMM_MAX_TILES) return GEMM_E_SHAPE;  // the scratch does not grow with the problem
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_E_HIP;
+  if (dev < 0 || dev >= kNoallocMaxDevices) return GEMM_E_DEVICE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+  NoallocDevice *d = nullptr;
+  st = noalloc_setup(dev, s, &d);
+  if (st != GEMM_OK) return st;
+  KernelArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.single.A = static_cast<const uint16_t *>(A);
+  args.single.B = static_cast<const uint16_t *>(B);
+  args.single.C = C;
+  args.single.M = (int32_t)M;
+  args.single.N = (int32_t)N;
+  args.single.K = (int32_t)K;
+  args.single.tiles_m = (int32_t)tm;
+  args.single.tiles_n = (int32_t)tn;
+  args.G = 1;
+  // the default plan's configuration (gemm_default_desc with tile edge 256)
+  const int64_t workers = (int64_t)d->occupancy * d->cu_count;
+  const int64_t grid = sched_mode == GEMM_SCHED_STATIC ? std::min<int64_t>(tiles, workers) : tiles;
+  args.T = (int32_t)tiles;
+  args.items = (int32_t)tiles;
+  args.claim_group = 1;
+  args.split_base = (int32_t)tiles;
+  args.split_chunks = 1;
+  args.P = (int32_t)grid;
+  args.claims_ahead = 1;
+  args.ring_depth = 3;
+  args.claim_lead = 4;
+  args.claim_policy = 1;
+  args.raster_group = 1;
+  args.k_rotation = kDefaultKRotation;
+  args.gate_spin_limit = kDefaultGateSpinLimit;
+  unsigned char *cur = d->ptr + (d->runs & 1u) * kNoallocSetBytes;
+  unsigned char *nxt = d->ptr + ((d->runs + 1) & 1u) * kNoallocSetBytes;
+  args.ctrl = reinterpret_cast<SchedCtrl *>(cur);
+  // no split tail and no log: the arrival and visit counters are never touched;
+  // they point at the unused rest of the set
+  args.arrivals = reinterpret_cast<uint32_t *>(cur + sizeof(SchedCtrl));
+  args.visits = reinterpret_cast<uint32_t *>(cur + sizeof(SchedCtrl));
+  args.ctrl_next = reinterpret_cast<SchedCtrl *>(nxt);
+  args.clear_next = nullptr;
+  args.clear_count = 0;
+  args.status = d_status ? d_status : reinterpret_cast<uint32_t *>(d->ptr + 2 * kNoallocSetBytes);
+  hipError_t e = ptg::launch_gemm(256, sched_mode, false, false, args, (int)grid, 0, s);
+  if (e != hipSuccess) return GEMM_E_HIP;
+  ++d->runs;
+  return GEMM_OK;
 }
 
 gemm_status gemm_run_grouped(int32_t G, const void *const *A, const void *const *B, float *const *C,

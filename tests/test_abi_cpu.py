@@ -60,6 +60,8 @@ def test_status_strings_and_defaults(lib):
 def test_null_arguments_are_rejected_before_any_hip_call(lib):
     assert lib.gemm_create(None, None) == -1
     assert lib.gemm_run(None, None, None, 8, 8, 8, 2, None, None) == -1
+    assert lib.gemm_run_noalloc(None, None, None, 8, 8, 8, 2, None, None) == -1
+    assert lib.gemm_run_noalloc(None, None, None, 8, 8, 8, 7, None, None) == -1
     assert lib.gemm_run_grouped(1, None, None, None, None, None, None, 2, None, None) == -1
     n = ctypes.c_size_t(0)
     assert lib.gemm_read_log(None, None, 0, ctypes.byref(n)) == -1
