@@ -2,9 +2,9 @@
 """Benchmark: bf16 GEMM TFLOP/s and % of MFMA peak on 8192^3; tail makespans.
 
 One step = one pass of the whole hot path: a gemm_run of the dynamic scheduler
-(atomic claim counter + LDS claim ring) on M = N = K = 8192, 256x256 tiles (K staged 32 deep),
-A and B i.i.d. N(0,1)/sqrt(K) in bf16, fp32 C, tile log on. Inputs are resident
-in HBM before timing starts. The kernel time is measured with HIP events on
+(atomic claim counters + LDS claim ring) on M = N = K = 8192, 256x256 tiles (K staged 32 deep,
+automatic K order), A and B i.i.d. N(0,1)/sqrt(K) in bf16, fp32 C, tile log on. Inputs are
+resident in HBM before timing starts. The kernel time is measured with HIP events on
 the stream the kernel is launched on.
 
 Printed: ONE JSON line with the contract fields, a `roofline` object for the
@@ -376,7 +376,11 @@ def main():
     ap.add_argument("--no-tail", action="store_true")
     ap.add_argument("--no-modes", action="store_true", help="skip timing the other schedulers")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (5 times) to scale the HBM byte counters")
+                    help="only run a plain device copy of MIB MiB (5 times, for the byte counters' scale), then "
+                         "time 20 more: the practical HBM ceiling")
+    ap.add_argument("--dispatch-clocks", action="store_true",
+                    help="only run the headline launches (--warmup + --steps, back to back, each on a plan of its "
+                         "own so every launch keeps its tile log) and print each launch's time and shader clock")
     ap.add_argument("--profile-workload", default="", metavar="NAME",
                     choices=["", "tail_255", "tail_256", "tail_257", "grouped_uneven"],
                     help="only run that workload (--steps times, after --warmup) for a profiler; "
@@ -424,7 +428,11 @@ def main():
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+        # timing (a profiler run counts the first 5 launches only: it filters on nothing, so keep them first)
+        stream = torch.cuda.current_stream()
+        ms = time_runs(lambda: dst.copy_(src), 20, 0, stream)
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 25,
+                          "copy_ms": ms, "copy_gbs_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
     import persistent_tiled_gemm_amd as ptg
     from workloads import make_workload
@@ -448,6 +456,29 @@ def main():
     info = ptg.gemm_plan_info_get(plan)
     khz = info["wallclock_khz"]
     flops = 2.0 * M * N * K
+
+    if args.dispatch_clocks:
+        # the headline's launches, back to back as timed, each on its own plan (so each keeps its log):
+        # per launch the kernel time (events around each launch) and the clock its tiles ran at
+        n = args.warmup + args.steps
+        plans = [ptg.gemm_create(**dict(fields, log_capacity=1024)) for _ in range(n)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i, pl in enumerate(plans):
+            ptg.gemm_run(A, B, C, pl, mode=args.mode, stream=stream)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        for i, pl in enumerate(plans):
+            rec = ptg.gemm_read_log(pl)
+            ran = rec[rec["visits"] > 0]
+            cyc = (ran["t1"] - ran["t0"]).astype(np.float64)
+            print(json.dumps({"launch": i + 1, "timed": i >= args.warmup, "us": evs[i].elapsed_time(evs[i + 1]) * 1e3,
+                              "clock_ghz": clock_from_log(rec, khz), "tile_cycles_median": float(np.median(cyc)),
+                              "makespan_us": makespan_from_log(rec, khz)["makespan_us"]}), flush=True)
+            pl.destroy()
+        plan.destroy()
+        return
 
     log(f"timing {args.mode}: warmup {args.warmup}, steps {args.steps}")
     ms = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=args.mode, stream=stream), args.steps, args.warmup, stream)
@@ -512,7 +543,8 @@ def main():
            "config": {"workload": "square_8192", "M": M, "N": N, "K": K, "tile": [256, 256, 32],
                       "sched": args.mode, "claim_policy": "xcd_counters" if args.claim_policy == 1 else "single_counter",
                       "claims_ahead": args.claims_ahead, "ring_depth": 3,
-                      "raster_group": args.raster_group, "tile_log": not args.no_log, "accumulate": "fp32",
+                      "raster_group": args.raster_group, "k_order": "auto (8192^3: one phase per XCD region)",
+                      "tile_log": not args.no_log, "accumulate": "fp32",
                       "output": "fp32"},
            "frac_peak": tflops / PEAK_BF16_TFLOPS, "roofline": roof,
            "modes": modes}
@@ -528,8 +560,20 @@ def main():
         out["mfma_ceiling"]["tflops_frac_achieved"] = tflops / out["mfma_ceiling"]["tflops"]
         ptg.gemm_mfma_probe(iters=40000, random_operands=True, mfma_block=32)
         out["mfma_ceiling"]["mfma_32x32x16"] = ptg.gemm_mfma_probe(iters=40000, random_operands=True, mfma_block=32)
+        # the memory-side counterpart: what plain streaming kernels reach (1 GiB, four times the last-level
+        # cache), the practical ceiling for the HBM-bound tail-boundary shapes below
+        out["hbm_ceiling"] = {"read_gbs": ptg.gemm_hbm_probe(1 << 30, "read", reps=20),
+                              "copy_gbs": ptg.gemm_hbm_probe(1 << 30, "copy", reps=20),
+                              "what": "plain streaming kernels over 1 GiB (16-byte non-temporal loads/stores per lane): "
+                                      "read once; copy counts bytes read + written"}
     if not args.no_tail:
         out["tail"] = run_tail_sections(ptg, torch, stream, khz, (p, A, B, C))
+        if "hbm_ceiling" in out:
+            ceil = out["hbm_ceiling"]["read_gbs"]
+            for r in out["tail"]["tail_boundary"].values():
+                for v in r.values():
+                    if "hbm_gbs" in v:
+                        v["frac_of_read_ceiling"] = v["hbm_gbs"] / ceil
     plan.destroy()
 
     if not args.no_cpu_baseline:

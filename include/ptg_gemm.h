@@ -97,6 +97,13 @@ typedef enum gemm_sched_mode {
   GEMM_SCHED_DYNAMIC = 2
 } gemm_sched_mode;
 
+/* K orders (gemm_tile_desc.k_rotation). */
+#define GEMM_KROT_AUTO 0
+#define GEMM_KROT_OFF 1
+#define GEMM_KROT_XCD 2
+#define GEMM_KROT_XCD2 3
+#define GEMM_KROT_UNIT 4
+
 /* Size limits (checked; GEMM_E_SHAPE beyond them). */
 #define GEMM_MAX_K (1 << 20)
 #define GEMM_MAX_N (1 << 22)
@@ -193,16 +200,25 @@ typedef enum gemm_sched_mode {
  *   k_rotation      the order a work unit walks its K range in (the sum is the
  *                   same; only the fp32 rounding order inside a tile changes,
  *                   and it depends on the unit id alone, so all schedulers give
- *                   bitwise the same C). 0 = from the first k-step to the last.
- *                   1 = rotated: unit u starts at k-step (u mod 8) / 8 of its
- *                   range and wraps around, so the eight XCD regions walk K at
- *                   eight different phases while the workgroups of one XCD,
- *                   which share operand panels through its L2, stay together.
- *                   2 = rotated by a phase per unit (a hash of its id). Spreading
- *                   the phases keeps the concurrent reads of all CUs from
- *                   sharing their low address bits, which holds memory
- *                   bandwidth well below what the part streams otherwise.
- *                   Ignored (0) for units whose K is not a multiple of 32.
+ *                   bitwise the same C). When every workgroup walks K from the
+ *                   same end, the concurrent reads of all CUs share their low
+ *                   address bits (the same column of every row of A), which
+ *                   holds memory bandwidth well below what the part streams
+ *                   otherwise; a rotation (unit u starts part-way into its range
+ *                   and wraps around) spreads them.
+ *                   GEMM_KROT_AUTO (0, the default): per launch, plain order
+ *                   for grouped runs; for a single GEMM two phases per XCD
+ *                   region with at most 8 tile columns (each XCD then reads 32
+ *                   distinct A panels at once), one phase per region otherwise
+ *                   (an XCD's tiles share A panels, which stay in step).
+ *                   GEMM_KROT_OFF: first k-step to last.
+ *                   GEMM_KROT_XCD: unit u starts at (u mod 8) / 8 of its range:
+ *                   the eight XCD regions walk K at eight phases while the
+ *                   workgroups of one XCD, which share operand panels through
+ *                   its L2, stay together.
+ *                   GEMM_KROT_XCD2: (u mod 16) / 16: two phases per region.
+ *                   GEMM_KROT_UNIT: a phase per unit (a hash of its id).
+ *                   Units whose K is not a multiple of 32 keep the plain order.
  */
 typedef struct gemm_tile_desc {
   int32_t bm, bn, bk;
@@ -317,8 +333,8 @@ gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t 
  * For callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc. The same product as
  * gemm_run with the plan gemm_default_desc(256) gives (256 x 256 tiles,
- * per-XCD claim counters, one claim ahead, log off, no split tail, no claim
- * groups, no concurrency gate, B as K x N), with no plan: the scheduler state
+ * per-XCD claim counters, one claim ahead, automatic K order, log off, no
+ * split tail, no claim groups, no concurrency gate, B as K x N), with no plan: the scheduler state
  * lives in a library-owned device array of 768 bytes per device (two control
  * sets and a status word), which each device keeps until the process ends. Its
  * size does not depend on M, N or K; sizes beyond the library limits are
@@ -455,6 +471,21 @@ gemm_status gemm_test_spoiler(int32_t device, int32_t n_wgs, int64_t spin_ns, vo
  */
 gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operands, int32_t mfma_block,
                             double *tflops_out, double *clock_ghz_out);
+
+/*
+ * Measurement helper (no page behind it; a fact about the part): the memory
+ * bandwidth a plain streaming kernel reaches on `device` (current), the
+ * practical ceiling beside the 8 TB/s data-sheet figure for the HBM-bound GEMM
+ * shapes. kind 0: read `bytes` once (16-byte non-temporal loads per lane,
+ * grid-stride, four workgroups of 256 threads per CU); kind 1: copy `bytes`
+ * (read and write, the same access). Synchronous: allocates its buffers (one,
+ * or two for a copy, of `bytes` each; the buffer is zero-filled), runs 3
+ * untimed and `reps` timed launches between events and frees them.
+ * *gbs_out receives bytes moved (read, or read + written) per second in GB/s.
+ * bytes must be a multiple of 4096 in [1 MiB, 16 GiB], reps in 1..1000, else
+ * GEMM_E_INVALID_ARG; GEMM_E_NOMEM if the buffers do not fit.
+ */
+gemm_status gemm_hbm_probe(int32_t device, int64_t bytes, int32_t kind, int32_t reps, double *gbs_out);
 
 #ifdef __cplusplus
 }

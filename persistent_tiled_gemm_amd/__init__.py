@@ -8,7 +8,7 @@ The function names are the C ABI's: gemm_default_desc, gemm_create, gemm_run,
 gemm_run_noalloc, gemm_run_grouped, gemm_read_log, gemm_sync, gemm_plan_info_get, gemm_destroy,
 gemm_status_str, gemm_last_hip_error, gemm_test_preset_counter,
 gemm_test_preset_gate, gemm_test_stream_cu_mask, gemm_test_stream_destroy,
-gemm_test_spoiler, gemm_mfma_probe. Tensors are torch device tensors: A and B
+gemm_test_spoiler, gemm_mfma_probe, gemm_hbm_probe. Tensors are torch device tensors: A and B
 bf16 (or int16 / uint16 views of bf16 bits), C float32, all contiguous; streams
 are torch.cuda streams (default: the current stream).
 """
@@ -38,7 +38,7 @@ STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_E_INVALID_ARG", -2: "GEMM_E_SHAPE", -3: 
 ABI_FUNCTIONS = ("gemm_default_desc", "gemm_create", "gemm_run", "gemm_run_noalloc", "gemm_run_grouped", "gemm_read_log",
                  "gemm_sync", "gemm_plan_info_get", "gemm_destroy", "gemm_status_str", "gemm_last_hip_error",
                  "gemm_test_preset_counter", "gemm_test_preset_gate", "gemm_test_stream_cu_mask",
-                 "gemm_test_stream_destroy", "gemm_test_spoiler", "gemm_mfma_probe")
+                 "gemm_test_stream_destroy", "gemm_test_spoiler", "gemm_mfma_probe", "gemm_hbm_probe")
 
 
 class PtgError(RuntimeError):
@@ -124,6 +124,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gemm_test_spoiler.argtypes = [i32, i32, i64, vp, vp, ctypes.c_double]
     lib.gemm_mfma_probe.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_double)]
+    lib.gemm_hbm_probe.argtypes = [i32, i64, i32, i32, ctypes.POINTER(ctypes.c_double)]
     for name in ABI_FUNCTIONS:
         if name not in ("gemm_status_str", "gemm_last_hip_error"):
             getattr(lib, name).restype = ctypes.c_int32
@@ -383,6 +384,15 @@ def gemm_mfma_probe(iters: int = 20000, random_operands: bool = True, mfma_block
                                         ctypes.byref(tf), ctypes.byref(ghz))
     _check(st, "gemm_mfma_probe")
     return {"tflops": tf.value, "clock_ghz": ghz.value}
+
+
+def gemm_hbm_probe(bytes_: int = 1 << 30, kind: str = "read", reps: int = 20, device: int = 0) -> float:
+    """gemm_hbm_probe: GB/s a plain streaming kernel reaches ('read': read once; 'copy': read + write)."""
+    gbs = ctypes.c_double(0.0)
+    st = load_library().gemm_hbm_probe(int(device), int(bytes_), {"read": 0, "copy": 1}[kind], int(reps),
+                                       ctypes.byref(gbs))
+    _check(st, "gemm_hbm_probe")
+    return gbs.value
 
 
 def bf16_from_bits(bits: np.ndarray, device="cuda"):

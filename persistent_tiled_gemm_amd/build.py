@@ -16,7 +16,7 @@ INCLUDE = os.path.join(REPO, "include")
 LIB_NAME = "libptg_gemm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["gemm_kernel.hip", "spoiler.hip", "mfma_probe.hip", "gemm_api.hip"]
+SOURCES = ["gemm_kernel.hip", "spoiler.hip", "mfma_probe.hip", "hbm_probe.hip", "gemm_api.hip"]
 
 # gfx950 only. Packed-fp32 VALU forms are disabled (hipcc makes them from plain
 # float code; some of their forms have produced wrong results on this part).

@@ -18,6 +18,14 @@
 #include "ptg_gemm.h"
 #include "ptg_internal.hpp"
 
+namespace ptg {
+// Memory-only probe (hbm_probe.hip): kind 0 reads `bytes` of src (zeros) into a
+// sum, kind 1 copies `bytes` from src to dst; `grid` workgroups of 256 threads,
+// 16 bytes per lane.
+hipError_t launch_hbm_probe(int kind, int grid, const void *src, void *dst, size_t bytes, float *sink,
+                            hipStream_t s);
+}  // namespace ptg
+
 using ptg::KernelArgs;
 using ptg::KernelProblem;
 using ptg::SchedCtrl;
@@ -139,7 +147,33 @@ constexpr size_t kArrivalsOffset = sizeof(SchedCtrl);
 constexpr size_t kVisitsOffset = sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)ptg::kMaxSplitTiles;
 
 // K order of the default plan (see gemm_tile_desc.k_rotation).
-constexpr int32_t kDefaultKRotation = 0;
+constexpr int32_t kDefaultKRotation = GEMM_KROT_AUTO;
+
+// The kernel's K order for a launch (0 = none, 1 = a phase per XCD region,
+// 2 = two phases per region, 3 = a phase per unit) from the plan's k_rotation.
+// Only A's reads camp on shared low address bits (a k-step reads one column of
+// every row of the tile's A panel, and every CU is at about the same k-step);
+// B's reads of different tiles fall on different columns anyway. The
+// automatic choice therefore follows how many distinct A panels one XCD reads
+// at once. Workgroup w runs on XCD w mod 8, so with at most 8 tile columns an
+// XCD's 32 concurrent tiles have 32 distinct A panels (every column of one
+// panel row lands on a different XCD): two phases per region split them in
+// halves that read different columns, at the price of reading the (shared)
+// B panel slices at two phases. With more tile columns an XCD's tiles share
+// A panels; one phase per region keeps them in step and still spreads the
+// eight XCDs over K. Grouped launches keep the plain order (their units share
+// panels within a problem; rotated, they measured slower).
+int32_t resolve_k_rotation(int32_t desc_value, bool grouped, int64_t N, int64_t bn) {
+  switch (desc_value) {
+    case GEMM_KROT_OFF: return 0;
+    case GEMM_KROT_XCD: return 1;
+    case GEMM_KROT_XCD2: return 2;
+    case GEMM_KROT_UNIT: return 3;
+    default: break;
+  }
+  if (grouped || N <= 0) return 0;
+  return ceil_div(N, bn) <= 8 ? 2 : 1;
+}
 
 // Polls of the concurrency gate before a workgroup gives up (each well under a
 // microsecond: a few seconds at most).
@@ -200,7 +234,7 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   args.claim_lead = p->desc.claim_lead;
   args.claim_policy = p->desc.claim_policy;
   args.raster_group = p->desc.raster == 1 ? p->desc.raster_group : 1;
-  args.k_rotation = p->desc.k_rotation;
+  args.k_rotation = resolve_k_rotation(p->desc.k_rotation, grouped, args.single.N, p->desc.bn);
   args.counter_base = 0;
   if (mode == GEMM_SCHED_DYNAMIC && p->preset_pending) {
     args.counter_base = p->preset;
@@ -352,7 +386,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
       d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT || d.group_order < 0 ||
       d.group_order > 1 || d.claim_group < 0 || d.claim_group > GEMM_MAX_CLAIM_GROUP || d.b_layout < 0 ||
-      d.b_layout > 1 || d.gate_spin_limit < 0 || d.k_rotation < 0 || d.k_rotation > 2)
+      d.b_layout > 1 || d.gate_spin_limit < 0 || d.k_rotation < GEMM_KROT_AUTO || d.k_rotation > GEMM_KROT_UNIT)
     return GEMM_E_INVALID_ARG;
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -519,7 +553,7 @@ gemm_status gemm_run_noalloc(const void *A, const void *B, float *C, int64_t M, 
   args.claim_lead = 4;
   args.claim_policy = 1;
   args.raster_group = 1;
-  args.k_rotation = kDefaultKRotation;
+  args.k_rotation = resolve_k_rotation(kDefaultKRotation, false, N, 256);
   args.gate_spin_limit = kDefaultGateSpinLimit;
   unsigned char *cur = d->ptr + (d->runs & 1u) * kNoallocSetBytes;
   unsigned char *nxt = d->ptr + ((d->runs + 1) & 1u) * kNoallocSetBytes;
@@ -876,6 +910,50 @@ gemm_status gemm_mfma_probe(int32_t device, int32_t iters, int32_t random_operan
   if (e1) (void)hipEventDestroy(e1);
   if (sink) (void)hipFree(sink);
   if (ticks) (void)hipFree(ticks);
+  return st;
+}
+
+gemm_status gemm_hbm_probe(int32_t device, int64_t bytes, int32_t kind, int32_t reps, double *gbs_out) {
+  if (!gbs_out || kind < 0 || kind > 1 || reps < 1 || reps > 1000) return GEMM_E_INVALID_ARG;
+  if (bytes < (1 << 20) || bytes > (int64_t)16 << 30 || (bytes % 4096) != 0) return GEMM_E_INVALID_ARG;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GEMM_E_HIP;
+  if (cur != device) return GEMM_E_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return GEMM_E_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_E_UNSUPPORTED;
+  const int grid = 4 * prop.multiProcessorCount;
+  void *src = nullptr, *dst = nullptr;
+  float *sink = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  gemm_status st = GEMM_OK;
+  float ms = 0.0f;
+  if (hipMalloc(&src, (size_t)bytes) != hipSuccess || (kind == 1 && hipMalloc(&dst, (size_t)bytes) != hipSuccess) ||
+      hipMalloc(&sink, sizeof(float) * (size_t)grid) != hipSuccess) {
+    st = GEMM_E_NOMEM;
+  } else if (hipMemset(src, 0, (size_t)bytes) != hipSuccess || hipEventCreate(&e0) != hipSuccess ||
+             hipEventCreate(&e1) != hipSuccess) {
+    st = GEMM_E_HIP;
+  } else {
+    bool ok = true;
+    for (int w = 0; w < 3 && ok; ++w) ok = ptg::launch_hbm_probe(kind, grid, src, dst, (size_t)bytes, sink, nullptr) == hipSuccess;
+    ok = ok && hipEventRecord(e0, nullptr) == hipSuccess;
+    for (int r = 0; r < reps && ok; ++r)
+      ok = ptg::launch_hbm_probe(kind, grid, src, dst, (size_t)bytes, sink, nullptr) == hipSuccess;
+    ok = ok && hipEventRecord(e1, nullptr) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+         hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+    if (!ok || ms <= 0.0f) st = GEMM_E_HIP;
+  }
+  if (st == GEMM_OK) {
+    // bytes moved: read once (kind 0), or read and written (kind 1)
+    const double moved = (double)bytes * (kind == 1 ? 2.0 : 1.0) * (double)reps;
+    *gbs_out = moved / ((double)ms * 1e-3) / 1e9;
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (src) (void)hipFree(src);
+  if (dst) (void)hipFree(dst);
+  if (sink) (void)hipFree(sink);
   return st;
 }
 

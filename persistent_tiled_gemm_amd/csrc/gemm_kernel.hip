@@ -450,10 +450,13 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     const int32_t nsteps = ke - kb;
     int32_t rot = 0;
     if (args.k_rotation != 0 && nsteps > 1 && K % CF::BK == 0) {
-      if (args.k_rotation == 1) {
-        // one phase per XCD region (unit id mod 8): the workgroups of one XCD,
-        // which share operand panels through its L2, keep walking K together
-        rot = (int32_t)((item % (uint32_t)kXcdRegions) * (uint32_t)nsteps / (uint32_t)kXcdRegions);
+      if (args.k_rotation == 1 || args.k_rotation == 2) {
+        // one phase per XCD region (item id mod 8; a plain launch sends item
+        // i to XCD i mod 8): the workgroups of one XCD, which share operand
+        // panels through its L2, keep walking K together. Or two phases per
+        // region (item id mod 16), half the range apart.
+        const uint32_t phases = args.k_rotation == 1 ? (uint32_t)kXcdRegions : 2u * kXcdRegions;
+        rot = (int32_t)((item % phases) * (uint32_t)nsteps / phases);
       } else {
         // a phase per unit (multiplicative hash of the item id)
         rot = (int32_t)(((item * 2654435761u) >> 16) % (uint32_t)nsteps);

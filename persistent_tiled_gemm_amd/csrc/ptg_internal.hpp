@@ -66,7 +66,7 @@ struct KernelArgs {
   int32_t claim_lead;           // prefetch claims are issued this many k-steps before a tile ends
   int32_t claim_policy;         // 0: one global counter; 1/2: per-XCD counters (interleaved / contiguous regions) with stealing
   int32_t raster_group;         // <= 1: row-major
-  int32_t k_rotation;           // K order per unit: 0 = kb..ke-1; 1 = rotated by a phase per XCD region; 2 = per unit
+  int32_t k_rotation;           // K order per unit: 0 = kb..ke-1; rotated by a phase per XCD region (1), two per region (2), per unit (3)
   uint32_t counter_base;        // added to every claim (failure forcing)
   int32_t max_concurrent;       // 0: no gate
   uint32_t gate_spin_limit;     // polls of the gate before a workgroup gives up (> 0)

@@ -75,6 +75,7 @@ def test_null_arguments_are_rejected_before_any_hip_call(lib):
     assert lib.gemm_last_hip_error(None) == b""
     assert lib.gemm_test_spoiler(0, 0, 1000, None, None, 0.0) == -1
     assert lib.gemm_mfma_probe(0, 100, 1, 16, None, None) == -1
+    assert lib.gemm_hbm_probe(0, 1 << 30, 0, 20, None) == -1
 
 
 def test_struct_layouts_match_the_binding(tmp_path):

@@ -24,3 +24,13 @@ def test_mfma_probe_rates_and_clock(block):
         ptg.gemm_mfma_probe(iters=0)
     with pytest.raises(ptg.PtgError):
         ptg.gemm_mfma_probe(iters=100, mfma_block=8)
+
+
+def test_hbm_probe_reports_a_plausible_bandwidth():
+    # a plain streaming read and copy over 1 GiB: well above 1 TB/s and below the 8 TB/s data-sheet peak
+    read = ptg.gemm_hbm_probe(1 << 30, "read", reps=5)
+    copy = ptg.gemm_hbm_probe(1 << 30, "copy", reps=5)
+    say(f"hbm probe: read {read:.0f} GB/s, copy {copy:.0f} GB/s")
+    assert 1000.0 < read < 8000.0 and 1000.0 < copy < 8000.0, (read, copy)
+    with pytest.raises(ptg.PtgError):
+        ptg.gemm_hbm_probe(1000, "read")          # not a multiple of 4096, under 1 MiB
