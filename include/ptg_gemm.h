@@ -283,6 +283,8 @@ typedef struct gemm_plan_info {
   int64_t last_grid;         /* grid size of the last run */
   int32_t last_mode;         /* scheduler of the last run (-1 before the first) */
   int32_t lds_bytes;         /* LDS per workgroup */
+  int32_t last_k_rotation;   /* K order of the last run as resolved: GEMM_KROT_OFF, _XCD, _XCD2 or _UNIT */
+  int32_t pad;
 } gemm_plan_info;
 
 /*

@@ -29,6 +29,9 @@ SCHED_STATIC = 1
 SCHED_DYNAMIC = 2
 MODES = {"nonpersistent": SCHED_NONPERSISTENT, "static": SCHED_STATIC, "dynamic": SCHED_DYNAMIC}
 
+# K orders (plan field k_rotation)
+KROT_AUTO, KROT_OFF, KROT_XCD, KROT_XCD2, KROT_UNIT = 0, 1, 2, 3, 4
+
 GEMM_OK = 0
 STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_E_INVALID_ARG", -2: "GEMM_E_SHAPE", -3: "GEMM_E_UNSUPPORTED",
                 -4: "GEMM_E_DEVICE", -5: "GEMM_E_HIP", -6: "GEMM_E_NOMEM", -7: "GEMM_E_TIMEOUT",
@@ -71,7 +74,7 @@ class PlanInfo(ctypes.Structure):
                 ("last_tiles", ctypes.c_int64), ("last_units", ctypes.c_int64), ("last_items", ctypes.c_int64), ("last_split_base", ctypes.c_int64),
                 ("last_split_chunks", ctypes.c_int32), ("last_claim_group", ctypes.c_int32),
                 ("last_grid", ctypes.c_int64), ("last_mode", ctypes.c_int32),
-                ("lds_bytes", ctypes.c_int32)]
+                ("lds_bytes", ctypes.c_int32), ("last_k_rotation", ctypes.c_int32), ("pad", ctypes.c_int32)]
 
 
 TILE_REC_DTYPE = np.dtype([("tile", "<u4"), ("worker", "<u4"), ("hw_id", "<u4"), ("xcc_id", "<u4"),

@@ -70,6 +70,7 @@ struct gemm_plan {
   int32_t last_claim_group = 1;
   int64_t last_grid = 0;
   int32_t last_mode = -1;
+  int32_t last_k_rotation = GEMM_KROT_OFF;
   std::vector<int32_t> last_tile_start;  // per problem (grouped), for log decoding
   std::vector<int32_t> last_k;           // K per problem, for log decoding
   std::vector<std::pair<int32_t, int32_t>> last_unit_map;  // grouped, claim order: (unit_start, tile_start)
@@ -270,6 +271,7 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   p->last_claim_group = group;
   p->last_grid = grid;
   p->last_mode = mode;
+  p->last_k_rotation = GEMM_KROT_OFF + args.k_rotation;  // kernel order 0..3 -> GEMM_KROT_OFF.._UNIT
   return GEMM_OK;
 }
 
@@ -759,6 +761,7 @@ gemm_status gemm_plan_info_get(gemm_tile_cfg tile_cfg, gemm_plan_info *out) {
   out->last_grid = p->last_grid;
   out->last_mode = p->last_mode;
   out->lds_bytes = p->lds_bytes;
+  out->last_k_rotation = p->last_k_rotation;
   return GEMM_OK;
 }
 
