@@ -378,6 +378,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times, for the byte counters' scale), then "
                          "time 20 more: the practical HBM ceiling")
+    ap.add_argument("--trace-out", default="", metavar="PATH",
+                    help="write the last timed headline launch's tile log as a Chrome trace (one event per tile "
+                         "on the timeline of the CU that ran it)")
     ap.add_argument("--dispatch-clocks", action="store_true",
                     help="only run the headline launches (--warmup + --steps, back to back, each on a plan of its "
                          "own so every launch keeps its tile log) and print each launch's time and shader clock")
@@ -483,7 +486,15 @@ def main():
     log(f"timing {args.mode}: warmup {args.warmup}, steps {args.steps}")
     ms = time_runs(lambda: ptg.gemm_run(A, B, C, plan, mode=args.mode, stream=stream), args.steps, args.warmup, stream)
     tflops = flops / (ms * 1e-3) / 1e12
-    clock_ghz = None if args.no_log else clock_from_log(ptg.gemm_read_log(plan), khz)
+    clock_ghz = None
+    if not args.no_log:
+        last_log = ptg.gemm_read_log(plan)
+        clock_ghz = clock_from_log(last_log, khz)
+        if args.trace_out:
+            from persistent_tiled_gemm_amd.trace import write_chrome_trace
+            n = write_chrome_trace(last_log, khz, args.trace_out, label="8192^3",
+                                   metadata={"workload": "square_8192", "sched": args.mode})
+            log(f"wrote {n} tile events to {args.trace_out}")
 
     modes = {}
     if not args.no_modes:
