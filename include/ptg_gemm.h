@@ -62,6 +62,17 @@
  * streams are ordered on the device (a run waits for the plan's previous
  * stream). A plan is not thread-safe.
  *
+ * Graph capture. gemm_run and gemm_run_noalloc enqueue one kernel and nothing
+ * else, and every run leaves the scheduler state it used (claim counters, gate,
+ * split-tile arrival counts) back at zero when it ends, so a captured launch
+ * can be replayed any number of times. Make a plan's first run on the capture
+ * stream before capturing (a run on a new stream first waits for the plan's
+ * previous stream with an event), and gemm_run_noalloc's first call on a
+ * device outside capture (it clears its state array then). With the tile log
+ * on, a replayed launch adds to the visit counts of the previous replay (the
+ * log is reset by the plan's next uncaptured run). Grouped runs upload their
+ * problem table and are not meant for capture.
+ *
  * Errors. Every call returns a gemm_status; 0 is success. Invalid arguments are
  * rejected before anything is enqueued. HIP failures return GEMM_E_HIP and the
  * HIP error text is kept in the plan (gemm_last_hip_error). Failures inside a

@@ -122,6 +122,23 @@ __device__ __forceinline__ void flag_error(const KernelArgs &a, uint32_t bit) {
   __hip_atomic_fetch_or(a.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Thread 0 of every workgroup, once, after its last use of the run's scheduler
+// state: count the workgroup out; the last one of the grid resets the claim
+// counters, the gate and the count itself, so the next launch that uses this
+// state set (the plan's run after next, or the same launch replayed from a
+// graph) starts from zero without a host-side reset.
+__device__ __forceinline__ void leave_run(const KernelArgs &a) {
+  const uint32_t done = __hip_atomic_fetch_add(&a.ctrl->exit_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (done + 1u == gridDim.x) {
+    __hip_atomic_store(&a.ctrl->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.ctrl->gate, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.ctrl->error, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int x = 0; x < kXcdRegions; ++x)
+      __hip_atomic_store(&a.ctrl->xcd_counter[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.ctrl->exit_count, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Ask the scheduler for an alternation of one MFMA and one LDS read in the
 // current scheduling region (then the remaining MFMAs or reads).
 template <int READS, int MFMAS>
@@ -258,6 +275,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     args.ctrl_next->counter = 0u;
     args.ctrl_next->gate = 0u;
     args.ctrl_next->error = 0u;
+    args.ctrl_next->exit_count = 0u;
     for (int x = 0; x < kXcdRegions; ++x) args.ctrl_next->xcd_counter[x] = 0u;
   }
   if (args.clear_count > 0) {
@@ -290,7 +308,10 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       gate_ok = ok;
     }
     __syncthreads();
-    if (!gate_ok) return;
+    if (!gate_ok) {
+      if (tid == 0) leave_run(args);
+      return;
+    }
   }
 
   // scalar reads, kept per wave (only wave 0's values are logged and used to claim)
@@ -903,6 +924,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       if (tid == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(&args.arrivals[q], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         split_last = prev + 1u == S ? 1u : 0u;
+        // every chunk has arrived: the count is done with for this run
+        if (prev + 1u == S) __hip_atomic_store(&args.arrivals[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
       if (wave_uniform(split_last) != 0) {
@@ -998,8 +1021,10 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     ++ord;
   }
 
-  if (args.max_concurrent > 0 && tid == 0) {
-    __hip_atomic_fetch_sub(&args.ctrl->gate, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    if (args.max_concurrent > 0)
+      __hip_atomic_fetch_sub(&args.ctrl->gate, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    leave_run(args);
   }
 }
 

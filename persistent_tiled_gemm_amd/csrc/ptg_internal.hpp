@@ -24,12 +24,16 @@ static constexpr int kXcdRegions = 8;
 
 // Scheduler state in device memory. A plan keeps two sets (control block +
 // visit counters); run i uses set i % 2 and clears set (i + 1) % 2 for the next
-// run, so a run is exactly one kernel launch with no host-side reset.
+// run, so a run is exactly one kernel launch with no host-side reset. Each run
+// also leaves its own set's counters at zero (the last workgroup to finish
+// resets them, and the last chunk of a split tile resets its arrival count), so
+// a captured launch replayed again and again on the same set starts clean too.
 struct alignas(64) SchedCtrl {
   uint32_t counter;    // dynamic claim counter (single-counter policy)
   uint32_t gate;       // workgroups currently holding a concurrency slot
   uint32_t error;      // bit 0: a gate wait ran out; bit 1: ring record for the wrong ordinal
-  uint32_t pad[5];
+  uint32_t exit_count; // workgroups of the run that have finished (the last one resets the counters)
+  uint32_t pad[4];
   uint32_t xcd_counter[kXcdRegions];  // per-XCD claim counters (XCD-partitioned policy)
 };
 static_assert(sizeof(SchedCtrl) == 64, "control block layout");
