@@ -122,6 +122,25 @@ __device__ __forceinline__ void flag_error(const KernelArgs &a, uint32_t bit) {
   __hip_atomic_fetch_or(a.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Rotation of a unit's K order: the physical k-step its logical step kb + i
+// reads is kb + ((i + rot) mod nsteps) (see the K order at the item set-up).
+__device__ __forceinline__ int32_t k_rotation_of(const KernelArgs &a, uint32_t item, int32_t nsteps) {
+  if (a.k_rotation == 0 || nsteps <= 1) return 0;
+  uint32_t rot;
+  if (a.k_rotation == 1 || a.k_rotation == 2) {
+    // one phase per XCD region (item id mod 8; a plain launch sends item i to
+    // XCD i mod 8): the workgroups of one XCD, which share operand panels
+    // through its L2, keep walking K together. Or two phases per region (item
+    // id mod 16), half the range apart.
+    const uint32_t phases = a.k_rotation == 1 ? (uint32_t)kXcdRegions : 2u * kXcdRegions;
+    rot = (item % phases) * (uint32_t)nsteps / phases;
+  } else {
+    // a phase per unit (multiplicative hash of the item id)
+    rot = ((item * 2654435761u) >> 16) % (uint32_t)nsteps;
+  }
+  return (int32_t)wave_uniform(rot);
+}
+
 // Thread 0 of every workgroup, once, after its last use of the run's scheduler
 // state: count the workgroup out; the last one of the grid resets the claim
 // counters, the gate and the count itself, so the next launch that uses this
@@ -469,21 +488,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // every scheduler still gives bitwise the same C). Off when K has a partial
     // k-step (the K-tail masking assumes that step comes last).
     const int32_t nsteps = ke - kb;
-    int32_t rot = 0;
-    if (args.k_rotation != 0 && nsteps > 1 && K % CF::BK == 0) {
-      if (args.k_rotation == 1 || args.k_rotation == 2) {
-        // one phase per XCD region (item id mod 8; a plain launch sends item
-        // i to XCD i mod 8): the workgroups of one XCD, which share operand
-        // panels through its L2, keep walking K together. Or two phases per
-        // region (item id mod 16), half the range apart.
-        const uint32_t phases = args.k_rotation == 1 ? (uint32_t)kXcdRegions : 2u * kXcdRegions;
-        rot = (int32_t)((item % phases) * (uint32_t)nsteps / phases);
-      } else {
-        // a phase per unit (multiplicative hash of the item id)
-        rot = (int32_t)(((item * 2654435761u) >> 16) % (uint32_t)nsteps);
-      }
-      rot = (int32_t)wave_uniform((uint32_t)rot);
-    }
+    const int32_t rot = K % CF::BK == 0 ? k_rotation_of(args, item, nsteps) : 0;
     // physical k-step of logical k-step kt (logical steps past ke read zeros
     // through a dead resource, whatever their base)
     auto phys = [&](int32_t kt) -> int32_t { return kt + rot >= ke ? kt + rot - nsteps : kt + rot; };
@@ -852,7 +857,10 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // the epilogue: reading an atomic's answer waits for every older memory
     // operation of the wave, and the C stores would otherwise be among them.
     auto publish_claims = [&]() {
-      wait_vmem_all();  // the answers of claims sent from assembly
+      // the answers of claims sent from assembly. A full drain: a returning
+      // atomic is not ordered with the loads issued after it, so only vmcnt 0
+      // proves its answer (and the register it writes) has arrived
+      wait_vmem_all();
       for (uint32_t b = 0; b < batch_n; ++b) {
         const uint32_t v = claim_resolve(args, xcc, lane, b == 0 ? batch[0] : batch[1], region);
         const uint32_t ok = v < (uint32_t)T ? 1u : 0u;
@@ -883,6 +891,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // displace the A and B slices the XCD's other workgroups are still reading
     // from L2 (measured 1-3% faster across the modes).
     const bool interior = m0 + BM <= M && n0 + BN <= N;
+
     auto store_group = [&](int mi, int ni, int qd, const f32x4 &v) {
       const int32_t m = m0 + (int32_t)(wm * CF::WM + mi * CF::MB + (lane % CF::MB));
       const int32_t n = n0 + (int32_t)(wn * CF::WN + ni * CF::MB + 8 * qd + 4 * (lane / CF::MB));
