@@ -217,18 +217,21 @@ typedef enum gemm_sched_mode {
  *                   holds memory bandwidth well below what the part streams
  *                   otherwise; a rotation (unit u starts part-way into its range
  *                   and wraps around) spreads them.
- *                   GEMM_KROT_AUTO (0, the default): per launch, plain order
- *                   for grouped runs; for a single GEMM two phases per XCD
- *                   region with at most 8 tile columns (each XCD then reads 32
- *                   distinct A panels at once), one phase per region otherwise
- *                   (an XCD's tiles share A panels, which stay in step).
+ *                   The phase follows a key: the unit id u in a single GEMM,
+ *                   the problem's index in a grouped run (its tiles share its
+ *                   operand panels and walk K together).
+ *                   GEMM_KROT_AUTO (0, the default): per launch; for a single
+ *                   GEMM two phases per XCD region with at most 8 tile columns
+ *                   (each XCD then reads 32 distinct A panels at once), one
+ *                   phase per region otherwise (an XCD's tiles share A panels,
+ *                   which stay in step); for a grouped run a phase per problem.
  *                   GEMM_KROT_OFF: first k-step to last.
- *                   GEMM_KROT_XCD: unit u starts at (u mod 8) / 8 of its range:
+ *                   GEMM_KROT_XCD: key u starts at (u mod 8) / 8 of its range:
  *                   the eight XCD regions walk K at eight phases while the
  *                   workgroups of one XCD, which share operand panels through
  *                   its L2, stay together.
  *                   GEMM_KROT_XCD2: (u mod 16) / 16: two phases per region.
- *                   GEMM_KROT_UNIT: a phase per unit (a hash of its id).
+ *                   GEMM_KROT_UNIT: a phase per key (a hash of it).
  *                   Units whose K is not a multiple of 32 keep the plain order.
  */
 typedef struct gemm_tile_desc {

@@ -151,19 +151,21 @@ constexpr size_t kVisitsOffset = sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)
 constexpr int32_t kDefaultKRotation = GEMM_KROT_AUTO;
 
 // The kernel's K order for a launch (0 = none, 1 = a phase per XCD region,
-// 2 = two phases per region, 3 = a phase per unit) from the plan's k_rotation.
-// Only A's reads camp on shared low address bits (a k-step reads one column of
-// every row of the tile's A panel, and every CU is at about the same k-step);
-// B's reads of different tiles fall on different columns anyway. The
-// automatic choice therefore follows how many distinct A panels one XCD reads
-// at once. Workgroup w runs on XCD w mod 8, so with at most 8 tile columns an
-// XCD's 32 concurrent tiles have 32 distinct A panels (every column of one
-// panel row lands on a different XCD): two phases per region split them in
-// halves that read different columns, at the price of reading the (shared)
-// B panel slices at two phases. With more tile columns an XCD's tiles share
-// A panels; one phase per region keeps them in step and still spreads the
-// eight XCDs over K. Grouped launches keep the plain order (their units share
-// panels within a problem; rotated, they measured slower).
+// 2 = two phases per region, 3 = a phase per key) from the plan's k_rotation.
+// The phase follows the item id in a single GEMM and the problem in a grouped
+// run. Only A's reads camp on shared low address bits (a k-step reads one
+// column of every row of the tile's A panel, and every CU is at about the same
+// k-step); B's reads of different tiles fall on different columns anyway. For a
+// single GEMM the automatic choice therefore follows how many distinct A panels
+// one XCD reads at once. Workgroup w runs on XCD w mod 8, so with at most 8
+// tile columns an XCD's 32 concurrent tiles have 32 distinct A panels (every
+// column of one panel row lands on a different XCD): two phases per region
+// split them in halves that read different columns, at the price of reading
+// the (shared) B panel slices at two phases. With more tile columns an XCD's
+// tiles share A panels; one phase per region keeps them in step and still
+// spreads the eight XCDs over K. A grouped run gets a phase per problem: a
+// problem's tiles, which share its panels, walk K together, and the problems
+// an XCD runs at once read different columns.
 int32_t resolve_k_rotation(int32_t desc_value, bool grouped, int64_t N, int64_t bn) {
   switch (desc_value) {
     case GEMM_KROT_OFF: return 0;
@@ -172,7 +174,8 @@ int32_t resolve_k_rotation(int32_t desc_value, bool grouped, int64_t N, int64_t 
     case GEMM_KROT_UNIT: return 3;
     default: break;
   }
-  if (grouped || N <= 0) return 0;
+  if (grouped) return 3;
+  if (N <= 0) return 0;
   return ceil_div(N, bn) <= 8 ? 2 : 1;
 }
 

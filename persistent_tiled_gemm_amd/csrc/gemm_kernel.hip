@@ -124,6 +124,7 @@ __device__ __forceinline__ void flag_error(const KernelArgs &a, uint32_t bit) {
 
 // Rotation of a unit's K order: the physical k-step its logical step kb + i
 // reads is kb + ((i + rot) mod nsteps) (see the K order at the item set-up).
+// `item` is the key the phase follows: the item id, or a grouped run's problem.
 __device__ __forceinline__ int32_t k_rotation_of(const KernelArgs &a, uint32_t item, int32_t nsteps) {
   if (a.k_rotation == 0 || nsteps <= 1) return 0;
   uint32_t rot;
@@ -393,8 +394,13 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     }
     KernelProblem pb;
     int32_t local = (int32_t)tile;
+    // what the K-order phase is keyed by: the item (single GEMMs), or the
+    // problem (grouped runs: its tiles share its operand panels, so they walk
+    // K in step, while different problems take different phases)
+    uint32_t rot_key = item;
     if constexpr (GROUPED) {
       const int32_t prob = find_problem(args.groups, args.G, (int32_t)tile);
+      rot_key = (uint32_t)prob;
       pb = args.groups[prob];
       // the descriptor is the same for the whole workgroup: keep it in SGPRs
       pb.A = uniform_ptr(pb.A);
@@ -488,7 +494,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // every scheduler still gives bitwise the same C). Off when K has a partial
     // k-step (the K-tail masking assumes that step comes last).
     const int32_t nsteps = ke - kb;
-    const int32_t rot = K % CF::BK == 0 ? k_rotation_of(args, item, nsteps) : 0;
+    const int32_t rot = K % CF::BK == 0 ? k_rotation_of(args, rot_key, nsteps) : 0;
     // physical k-step of logical k-step kt (logical steps past ke read zeros
     // through a dead resource, whatever their base)
     auto phys = [&](int32_t kt) -> int32_t { return kt + rot >= ke ? kt + rot - nsteps : kt + rot; };

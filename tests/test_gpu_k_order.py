@@ -104,7 +104,7 @@ def test_k_orders_with_a_split_tail():
 
 
 def test_automatic_k_order():
-    # at most 8 tile columns: two phases per XCD region; more: one; grouped runs: none
+    # at most 8 tile columns: two phases per XCD region; more: one; grouped runs: a phase per problem
     import torch
     plan = make_plan(256)
     assert plan.desc.k_rotation == ptg.KROT_AUTO
@@ -120,5 +120,34 @@ def test_automatic_k_order():
     C = torch.empty((q.M, q.N), dtype=torch.float32, device="cuda")
     ptg.gemm_run_grouped([A, A], [B, B], [C, C.clone()], plan, mode="dynamic")
     torch.cuda.synchronize()
-    assert ptg.gemm_plan_info_get(plan)["last_k_rotation"] == ptg.KROT_OFF
+    assert ptg.gemm_plan_info_get(plan)["last_k_rotation"] == ptg.KROT_UNIT   # a phase per problem
+    plan.destroy()
+
+
+@pytest.mark.parametrize("order", list(ORDERS))
+def test_every_k_order_in_grouped_runs(order):
+    # grouped runs key the phase to the problem: every order matches the oracle on ragged problems and
+    # gives bitwise the same C under every scheduler
+    import torch
+    shapes = [(300, 264, 512), (520, 776, 1024), (256, 256, 96), (700, 520, 2048), (64, 1032, 256)]
+    problems = [make_problem(M, N, K, "normal", seed=90 + i) for i, (M, N, K) in enumerate(shapes)]
+    As = [ptg.bf16_from_bits(q.a_bits) for q in problems]
+    Bs = [ptg.bf16_from_bits(q.b_bits) for q in problems]
+    plan = make_plan(256, k_rotation=ORDERS[order], group_order=1, claim_policy=2)
+    T = sum(-(-M // 256) * -(-N // 256) for M, N, _ in shapes)
+    outs = {}
+    for mode in MODES:
+        say(f"case grouped k order {order} mode={mode}")
+        Cs = [torch.full((q.M, q.N), float("nan"), dtype=torch.float32, device="cuda") for q in problems]
+        ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode)
+        torch.cuda.synchronize()
+        info = ptg.gemm_plan_info_get(plan)
+        assert info["last_k_rotation"] == ORDERS[order]
+        check_log(plan, mode, T, P=info["last_grid"] if mode == "static" else None)
+        outs[mode] = [c.cpu().numpy() for c in Cs]
+    for q, c in zip(problems, outs["dynamic"]):
+        assert_close_rows(q, c, range(q.M))
+    for g in range(len(problems)):
+        assert np.array_equal(outs["static"][g], outs["dynamic"][g])
+        assert np.array_equal(outs["nonpersistent"][g], outs["dynamic"][g])
     plan.destroy()
