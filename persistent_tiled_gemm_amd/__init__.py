@@ -405,6 +405,30 @@ def bf16_from_bits(bits: np.ndarray, device="cuda"):
     return t.to(device).view(torch.bfloat16)
 
 
+def gemm(A, B, C=None, mode="dynamic", plan: Optional[Plan] = None, stream=None):
+    """C = A.B through gemm_run (A: M x K bf16, B: K x N bf16; with a plan of b_layout 1, B is N x K).
+
+    C (optional) is an M x N float32 device tensor to overwrite; it is allocated when absent. The run goes on
+    `stream` (default: the current stream). With no plan, a default 256 x 256 plan is made for the call, the
+    call waits for the run and raises PtgError on a device-side failure too; with a caller's plan it returns
+    at once (check the plan with gemm_sync). Returns C."""
+    import torch
+    own = plan is None
+    if own:
+        plan = gemm_create()
+    try:
+        n = B.shape[1] if int(plan.desc.b_layout) == 0 else B.shape[0]
+        if C is None:
+            C = torch.empty((A.shape[0], n), dtype=torch.float32, device=A.device)
+        gemm_run(A, B, C, plan, mode=mode, stream=stream)
+        if own:
+            gemm_sync(plan)
+    finally:
+        if own:
+            plan.destroy()
+    return C
+
+
 def matmul(A, B, mode="dynamic", plan: Optional[Plan] = None, stream=None):
     """Convenience: allocate C and run C = A.B with a default 256x256 plan."""
     import torch

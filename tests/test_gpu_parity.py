@@ -285,3 +285,24 @@ def test_k_tail_on_every_trip_boundary(K):
     assert np.array_equal(outs["static"], outs["dynamic"])
     assert np.array_equal(outs["nonpersistent"], outs["dynamic"])
     plan.destroy()
+
+
+def test_python_gemm_entry():
+    # ptg.gemm(A, B, C=None, mode, plan): allocates C when absent, writes a given C in place, checks operands
+    torch = torch_mod()
+    p = make_problem(520, 264, 1000, "uniform", seed=51)
+    A, B = ptg.bf16_from_bits(p.a_bits), ptg.bf16_from_bits(p.b_bits)
+    for mode in MODES:
+        say(f"case ptg.gemm mode={mode}")
+        c = ptg.gemm(A, B, mode=mode)
+        assert_close_full(p, c.cpu().numpy())
+    C = torch.full((p.M, p.N), float("nan"), dtype=torch.float32, device="cuda")
+    plan = make_plan(256, log_capacity=0)
+    assert ptg.gemm(A, B, C, plan=plan) is C
+    ptg.gemm_sync(plan)
+    assert_close_full(p, C.cpu().numpy())
+    with pytest.raises(ValueError):
+        ptg.gemm(A.float(), B)                  # wrong dtype
+    with pytest.raises(ValueError):
+        ptg.gemm(A, B[:, :200])                  # not contiguous
+    plan.destroy()
