@@ -60,7 +60,9 @@
  * here synchronises except gemm_sync, gemm_read_log, gemm_destroy and
  * gemm_test_spoiler's optional residency wait. Runs of one plan on different
  * streams are ordered on the device (a run waits for the plan's previous
- * stream). A plan is not thread-safe.
+ * stream). The plan keeps the stream of its last run: that stream must stay
+ * valid until the plan's next run, gemm_sync, gemm_read_log or gemm_destroy,
+ * which use it. A plan is not thread-safe.
  *
  * Graph capture. gemm_run and gemm_run_noalloc enqueue one kernel and nothing
  * else, and every run leaves the scheduler state it used (claim counters, gate,

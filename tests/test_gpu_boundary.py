@@ -131,8 +131,8 @@ def test_cu_masked_stream_confines_the_kernel(mode):
         assert 0 < len(used) <= allowed
         assert_close_full(p, C.cpu().numpy())
     finally:
+        plan.destroy()        # synchronises the plan's last stream, the masked one, while it is still valid
         stream.destroy()
-        plan.destroy()
 
 
 def test_cu_mask_arguments_are_checked():
