@@ -76,12 +76,19 @@ def time_runs(fn, steps: int, warmup: int, stream):
     return start.elapsed_time(end) / steps  # ms per step
 
 
-def time_interleaved(fns, rounds: int, per_round: int, stream):
+def time_interleaved(fns, rounds: int, per_round: int, stream, warm: int = 10):
     """Mean ms per call of each function, timed in `rounds` blocks of `per_round` calls per function,
     the order of the functions alternating between rounds; each block starts with three untimed calls
-    (the first call after a switch or an idle gap reads slow)."""
+    (the first call after a switch or an idle gap reads slow). Before the first block every function
+    runs `warm` times: the first launches over freshly allocated operands read several percent slow
+    (measured on the tail-boundary shape: 153-165 us against 144-148 us from then on)."""
+    import torch
     total = {k: 0.0 for k in fns}
     names = list(fns)
+    for k in names:
+        for _ in range(warm):
+            fns[k]()
+    torch.cuda.synchronize()
     for r in range(rounds):
         for k in (names if r % 2 == 0 else names[::-1]):
             total[k] += time_runs(fns[k], per_round, 3, stream) * per_round

@@ -192,3 +192,21 @@ def test_fast_trips_compute_no_load_masks(asm, mode, grouped, bt):
     assert sorted(v for m, v in valu if m == 256) == [0] * runs, valu
     two = sorted(v for m, v in valu if m == 128)
     assert len(two) == 2 * runs and all(v <= 24 for v in two[:runs]) and all(v > 24 for v in two[runs:]), valu
+
+
+def test_no_kernel_uses_scratch(asm):
+    """No kernel of the library spills to scratch memory, in its main loop or anywhere else (a
+    spilled epilogue made the 256 x 256 tile several percent slower)."""
+    sizes = re.findall(r"\.amdhsa_kernel (\S+).*?\.amdhsa_private_segment_fixed_size (\d+)", asm, re.S)
+    assert len(sizes) >= len(ALL_CASES)
+    assert not [k for k, s in sizes if int(s) != 0]
+
+
+@pytest.mark.parametrize("mode,grouped,bt", ALL_CASES)
+def test_epilogue_stages_accumulators_through_lds(asm, mode, grouped, bt):
+    """The epilogue of a whole tile writes each accumulator quad to LDS straight from its AGPRs
+    (two passes of 32 quads per wave, no copies through VGPRs) and stores C in whole rows."""
+    body = instructions(kernel_lines(asm, mode, grouped, bt))
+    agpr_writes = [x for x in body if x.startswith("ds_write_b128") and ", a[" in x]
+    assert len(agpr_writes) == 64
+    assert not [x for x in body if x.startswith("v_accvgpr_read")]
