@@ -14,14 +14,17 @@
  *   GEMM_SCHED_NONPERSISTENT  grid = all tiles; block b computes tile b and exits.
  *   GEMM_SCHED_STATIC         grid = P workers; worker i computes i, i+P, i+2P, ...
  *                             (section "why a fixed task sequence tails").
- *   GEMM_SCHED_DYNAMIC        grid = all tiles (launch slots); every workgroup takes
- *                             tiles from atomic claim counters, the claim of the next
- *                             tile is prefetched through a ring of response records in
- *                             LDS (depth 3), a failed claim ends the worker,
- *                             late-launched slots exit after one failed claim. This
- *                             replaces the hardware launch-cancel of the blog post
- *                             (sections "cancelling the launch ..." and "following
- *                             the CUTLASS source"), which gfx950 lacks.
+ *   GEMM_SCHED_DYNAMIC        grid = min(tiles, workgroups resident at once); every
+ *                             workgroup takes tiles from atomic claim counters, the
+ *                             claim of the next tile is prefetched through a ring of
+ *                             response records in LDS (depth 3), a failed claim ends
+ *                             the worker, and a workgroup that starts after every
+ *                             tile is handed out exits at once. This replaces the
+ *                             hardware launch-cancel of the blog post (sections
+ *                             "cancelling the launch ..." and "following the CUTLASS
+ *                             source"), which gfx950 lacks; without it, launch slots
+ *                             beyond the resident workgroups would only start as the
+ *                             workers exit and leave again, so the grid stops there.
  *
  * Claim counters of the dynamic mode (plan field claim_policy):
  *   0  one device-wide counter hands out every tile id in order: the pages' single
