@@ -740,8 +740,12 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         // hold accumulators, and with the builtin the register allocator
         // rotated some through copies every trip). The statements are volatile
         // and clobber memory, so program order is issue order: MFMA i, then
-        // fragment read i of the next k-step (24 reads), the loads spread
-        // between the reads. Hazards: within the loop the MFMA operands are
+        // fragment read i of the next k-step (24 reads), and the eight loads
+        // of k-step kt + 4 after MFMAs 3, 10, ..., 52 (one every seven: spread
+        // over the step, they hold the MFMA stream least; measured against one
+        // after every third read, 302k against 317k cycles per 8192^3 tile and
+        // 3-4% off the HBM-bound shapes; all eight together after the first
+        // MFMA cost 392k). Hazards: within the loop the MFMA operands are
         // written only by LDS reads (waited for), and accumulators are written
         // only by MFMAs; the fences before and after the loop give the wait
         // states the compiler cannot see.
@@ -789,12 +793,15 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
                   bn[ni] = __builtin_bit_cast(bf16x8, v);
                 }
               }
-#pragma unroll
-              for (int j = 0; j < kLoads; ++j)
-                if (j * kReads / kLoads == r)
-                  load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j, st),
-                                decltype(fast)::value ? voff_fast[j] : load_voff(j, kt_load));
             }
+            // (a spacing of eight, which lines the loads up with the rows of the
+            // accumulator grid, made the compiler give up unrolling the step)
+            static_assert(3 + 7 * (kLoads - 1) < kMfma, "load placement");
+#pragma unroll
+            for (int j = 0; j < kLoads; ++j)
+              if (3 + 7 * j == i)
+                load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j, st),
+                              decltype(fast)::value ? voff_fast[j] : load_voff(j, kt_load));
           }
           wait_lds_all();
           asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
