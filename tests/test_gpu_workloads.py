@@ -82,6 +82,11 @@ def test_tail_boundary(name, T):
         log = check_log(plan, mode, T, P=info["last_grid"] if mode == "static" else None)
         if mode == "static":
             assert info["last_grid"] == min(T, info["static_workers"])
+        elif mode == "dynamic":
+            # as many workgroups as can be resident at once, at most one per tile
+            assert info["last_grid"] == min(T, info["occupancy"] * info["cu_count"])
+        else:
+            assert info["last_grid"] == T
         full = C.cpu().numpy()
         assert not np.isnan(full).any()
         _check_rows(p, full, rows)

@@ -210,3 +210,22 @@ def test_epilogue_stages_accumulators_through_lds(asm, mode, grouped, bt):
     agpr_writes = [x for x in body if x.startswith("ds_write_b128") and ", a[" in x]
     assert len(agpr_writes) == 64
     assert not [x for x in body if x.startswith("v_accvgpr_read")]
+
+
+@pytest.mark.parametrize("mode,grouped,bt", ALL_CASES)
+def test_loads_are_spread_over_the_step(asm, mode, grouped, bt):
+    """The direct-to-LDS loads of a k-step sit apart from each other in the MFMA stream (one every
+    seven MFMAs): loads bunched together hold the MFMA stream (measured 392k against 302k cycles
+    per 8192^3 tile with all eight of a step after its first MFMA)."""
+    for body in loop_blocks(kernel_lines(asm, mode, grouped, bt), split_asm_labels=True):
+        mfma_seen = 0
+        last_load_at = None
+        gaps = []
+        for x in body:
+            if x.startswith("v_mfma"):
+                mfma_seen += 1
+            elif x.startswith("buffer_load_dwordx4") and x.endswith("lds"):
+                if last_load_at is not None:
+                    gaps.append(mfma_seen - last_load_at)
+                last_load_at = mfma_seen
+        assert gaps and min(gaps) >= 6, gaps
