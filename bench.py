@@ -508,9 +508,12 @@ def main():
         other = dict(fields, claim_policy=1 - args.claim_policy)
         plan_other = ptg.gemm_create(**other)
         plan_group = ptg.gemm_create(**dict(fields, claim_group=4, raster=1, raster_group=2))
+        # the dynamic grid stopping at the resident workgroups instead of one launch slot per tile
+        plan_resident = ptg.gemm_create(**dict(fields, dynamic_grid=ptg.GRID_RESIDENT))
         runs = [("nonpersistent", "nonpersistent", plan), ("static", "static", plan), ("dynamic", "dynamic", plan),
                 ("dynamic_single_counter" if args.claim_policy == 1 else "dynamic_xcd_counters", "dynamic", plan_other),
-                ("dynamic_claim_groups_2x2", "dynamic", plan_group)]
+                ("dynamic_claim_groups_2x2", "dynamic", plan_group),
+                ("dynamic_resident_grid", "dynamic", plan_resident)]
         fns = {name: (lambda mode=mode, pl=pl: ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream))
                for name, mode, pl in runs}
         # the same product with B given as N x K (plan b_layout 1: C = A . Bt^T)
@@ -542,6 +545,7 @@ def main():
                 modes[name].update(makespan_us=mk["makespan_us"], tile_median_us=mk["tile_median_us"])
         plan_other.destroy()
         plan_group.destroy()
+        plan_resident.destroy()
         plan_bt.destroy()
         del Bt
 

@@ -14,17 +14,15 @@
  *   GEMM_SCHED_NONPERSISTENT  grid = all tiles; block b computes tile b and exits.
  *   GEMM_SCHED_STATIC         grid = P workers; worker i computes i, i+P, i+2P, ...
  *                             (section "why a fixed task sequence tails").
- *   GEMM_SCHED_DYNAMIC        grid = min(tiles, workgroups resident at once); every
- *                             workgroup takes tiles from atomic claim counters, the
- *                             claim of the next tile is prefetched through a ring of
- *                             response records in LDS (depth 3), a failed claim ends
- *                             the worker, and a workgroup that starts after every
- *                             tile is handed out exits at once. This replaces the
+ *   GEMM_SCHED_DYNAMIC        grid = all tiles (launch slots; see dynamic_grid for
+ *                             the resident-only grid); every workgroup takes tiles
+ *                             from atomic claim counters, the claim of the next tile
+ *                             is prefetched through a ring of response records in
+ *                             LDS (depth 3), a failed claim ends the worker, and
+ *                             late-launched slots exit at once. This replaces the
  *                             hardware launch-cancel of the blog post (sections
  *                             "cancelling the launch ..." and "following the CUTLASS
- *                             source"), which gfx950 lacks; without it, launch slots
- *                             beyond the resident workgroups would only start as the
- *                             workers exit and leave again, so the grid stops there.
+ *                             source"), which gfx950 lacks.
  *
  * Claim counters of the dynamic mode (plan field claim_policy):
  *   0  one device-wide counter hands out every tile id in order: the pages' single
@@ -119,6 +117,10 @@ typedef enum gemm_sched_mode {
 #define GEMM_KROT_XCD 2
 #define GEMM_KROT_XCD2 3
 #define GEMM_KROT_UNIT 4
+
+/* Launch grid of the dynamic mode (gemm_tile_desc.dynamic_grid). */
+#define GEMM_GRID_ALL 0
+#define GEMM_GRID_RESIDENT 1
 
 /* Size limits (checked; GEMM_E_SHAPE beyond them). */
 #define GEMM_MAX_K (1 << 20)
@@ -238,6 +240,18 @@ typedef enum gemm_sched_mode {
  *                   GEMM_KROT_XCD2: (u mod 16) / 16: two phases per region.
  *                   GEMM_KROT_UNIT: a phase per key (a hash of it).
  *                   Units whose K is not a multiple of 32 keep the plain order.
+ *   dynamic_grid    the dynamic mode's grid. GEMM_GRID_ALL (0, the default):
+ *                   one launch slot per work unit, as the blog post's
+ *                   launch-cancel scheduler has; slots that start after every
+ *                   unit is handed out exit at once. GEMM_GRID_RESIDENT: only as
+ *                   many workgroups as can be resident at once (occupancy x CUs,
+ *                   at most one per unit). Without launch cancel, the slots of
+ *                   the full grid beyond the resident ones can only start as the
+ *                   workers exit, and then leave again: about 13-17 us per
+ *                   launch of 1024 tiles with the per-XCD counters (which probe
+ *                   every region before a slot gives up), 2-6 us with one
+ *                   counter. The schedule is the same either way (the counters
+ *                   decide who takes which unit).
  */
 typedef struct gemm_tile_desc {
   int32_t bm, bn, bk;
@@ -259,6 +273,7 @@ typedef struct gemm_tile_desc {
   int32_t b_layout;
   int32_t gate_spin_limit;
   int32_t k_rotation;
+  int32_t dynamic_grid;
 } gemm_tile_desc;
 
 /* Opaque plan: the tile_cfg argument of gemm_run. Owns all library scratch. */

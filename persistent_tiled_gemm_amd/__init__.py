@@ -31,6 +31,7 @@ MODES = {"nonpersistent": SCHED_NONPERSISTENT, "static": SCHED_STATIC, "dynamic"
 
 # K orders (plan field k_rotation)
 KROT_AUTO, KROT_OFF, KROT_XCD, KROT_XCD2, KROT_UNIT = 0, 1, 2, 3, 4
+GRID_ALL, GRID_RESIDENT = 0, 1  # gemm_tile_desc.dynamic_grid
 
 GEMM_OK = 0
 STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_E_INVALID_ARG", -2: "GEMM_E_SHAPE", -3: "GEMM_E_UNSUPPORTED",
@@ -57,7 +58,7 @@ class TileDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bm", "bn", "bk", "ring_depth", "claims_ahead", "claim_lead", "claim_policy", "raster", "raster_group", "static_workers",
         "log_capacity", "min_lds_bytes", "max_concurrent", "max_groups", "device", "tail_split", "group_order", "claim_group",
-        "b_layout", "gate_spin_limit", "k_rotation")]
+        "b_layout", "gate_spin_limit", "k_rotation", "dynamic_grid")]
 
 
 class TileRec(ctypes.Structure):

@@ -224,14 +224,13 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   plan_units(p, grouped, mode, tiles, K, &items, &split_base, &chunks, &group);
   if (items > GEMM_MAX_TILES) return GEMM_E_SHAPE;
   const int64_t units = ceil_div(items, group);
-  // Non-persistent: one workgroup per unit. Static: P workers. Dynamic: as many
-  // workgroups as can be resident at once, at most one per unit. (A grid of one
-  // workgroup per unit, as a launch-cancel scheduler would have, only adds
-  // workgroups that launch as the persistent workers exit, find every unit
-  // handed out and leave: 13-17 us per 8192^3 launch of 1024 tiles, measured.)
+  // Non-persistent: one workgroup per unit. Static: P workers. Dynamic: one
+  // launch slot per unit, or (GEMM_GRID_RESIDENT) only the workgroups that can
+  // be resident at once.
   int64_t grid = units;
   if (mode == GEMM_SCHED_STATIC) grid = std::min<int64_t>(units, p->static_workers);
-  if (mode == GEMM_SCHED_DYNAMIC) grid = std::min<int64_t>(units, (int64_t)p->occupancy * p->cu_count);
+  if (mode == GEMM_SCHED_DYNAMIC && p->desc.dynamic_grid == GEMM_GRID_RESIDENT)
+    grid = std::min<int64_t>(units, (int64_t)p->occupancy * p->cu_count);
   args.T = (int32_t)units;
   args.items = (int32_t)items;
   args.claim_group = group;
@@ -382,6 +381,7 @@ gemm_status gemm_default_desc(gemm_tile_desc *out, int32_t tile_edge, int32_t de
   out->b_layout = 0;
   out->gate_spin_limit = 0;
   out->k_rotation = kDefaultKRotation;
+  out->dynamic_grid = GEMM_GRID_ALL;
   return GEMM_OK;
 }
 
@@ -397,7 +397,8 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
       d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT || d.group_order < 0 ||
       d.group_order > 1 || d.claim_group < 0 || d.claim_group > GEMM_MAX_CLAIM_GROUP || d.b_layout < 0 ||
-      d.b_layout > 1 || d.gate_spin_limit < 0 || d.k_rotation < GEMM_KROT_AUTO || d.k_rotation > GEMM_KROT_UNIT)
+      d.b_layout > 1 || d.gate_spin_limit < 0 || d.k_rotation < GEMM_KROT_AUTO || d.k_rotation > GEMM_KROT_UNIT ||
+      d.dynamic_grid < GEMM_GRID_ALL || d.dynamic_grid > GEMM_GRID_RESIDENT)
     return GEMM_E_INVALID_ARG;
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -552,7 +553,7 @@ gemm_status gemm_run_noalloc(const void *A, const void *B, float *C, int64_t M, 
   args.G = 1;
   // the default plan's configuration (gemm_default_desc with tile edge 256)
   const int64_t workers = (int64_t)d->occupancy * d->cu_count;
-  const int64_t grid = sched_mode == GEMM_SCHED_NONPERSISTENT ? tiles : std::min<int64_t>(tiles, workers);
+  const int64_t grid = sched_mode == GEMM_SCHED_STATIC ? std::min<int64_t>(tiles, workers) : tiles;
   args.T = (int32_t)tiles;
   args.items = (int32_t)tiles;
   args.claim_group = 1;

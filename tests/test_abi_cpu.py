@@ -51,10 +51,20 @@ def test_status_strings_and_defaults(lib):
     d = ptg.gemm_default_desc(256, 0)
     assert (d.bm, d.bn, d.bk, d.ring_depth, d.claims_ahead, d.claim_lead, d.claim_policy) == (256, 256, 32, 3, 1, 4, 1)
     assert (d.log_capacity, d.max_concurrent, d.gate_spin_limit, d.tail_split, d.claim_group) == (0, 0, 0, 0, 1)
+    assert (d.k_rotation, d.dynamic_grid) == (ptg.KROT_AUTO, ptg.GRID_ALL)   # one launch slot per tile
     d = ptg.gemm_default_desc(128, 0)
     assert (d.bm, d.bn) == (128, 128)
     with pytest.raises(ptg.PtgError):
         ptg.gemm_default_desc(192, 0)
+
+
+def test_descriptor_values_out_of_range_are_rejected_before_any_hip_call(lib):
+    for field, bad in (("dynamic_grid", 2), ("dynamic_grid", -1), ("k_rotation", 5), ("claim_policy", 3)):
+        d = ptg.gemm_default_desc(256, 0)
+        setattr(d, field, bad)
+        out = ctypes.c_void_p()
+        assert lib.gemm_create(ctypes.byref(out), ctypes.byref(d)) == -1, field
+        assert not out.value
 
 
 def test_null_arguments_are_rejected_before_any_hip_call(lib):

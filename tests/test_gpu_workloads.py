@@ -82,14 +82,24 @@ def test_tail_boundary(name, T):
         log = check_log(plan, mode, T, P=info["last_grid"] if mode == "static" else None)
         if mode == "static":
             assert info["last_grid"] == min(T, info["static_workers"])
-        elif mode == "dynamic":
-            # as many workgroups as can be resident at once, at most one per tile
-            assert info["last_grid"] == min(T, info["occupancy"] * info["cu_count"])
         else:
-            assert info["last_grid"] == T
+            assert info["last_grid"] == T   # one launch slot per tile
         full = C.cpu().numpy()
         assert not np.isnan(full).any()
         _check_rows(p, full, rows)
+    # the dynamic grid stopping at the resident workgroups: same exactly-once log, same C
+    rplan = ptg.gemm_create(tile_edge=256, log_capacity=512, dynamic_grid=ptg.GRID_RESIDENT)
+    say(f"case {name} dynamic, resident grid")
+    C.fill_(float("nan"))
+    ptg.gemm_run(A, B, C, rplan, mode="dynamic")
+    torch.cuda.synchronize()
+    info = ptg.gemm_plan_info_get(rplan)
+    assert info["last_grid"] == min(T, info["occupancy"] * info["cu_count"])
+    check_log(rplan, "dynamic", T)
+    full = C.cpu().numpy()
+    assert not np.isnan(full).any()
+    _check_rows(p, full, rows)
+    rplan.destroy()
     plan.destroy()
 
 
