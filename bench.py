@@ -264,7 +264,7 @@ def run_tail_sections(ptg, torch, stream, khz, square):
         if name == "static":
             ran = rec[rec["visits"] > 0]
             dur = ((ran["r1"] - ran["r0"]).astype(np.float64) / khz * 1e3)
-            kt = ks[ran["problem"]] / 64.0
+            kt = ks[ran["problem"]] / 32.0   # 32-deep k-steps, the kernel's unit of K
             alpha, beta = np.polyfit(kt, dur, 1)
     res["cost_fit_us"] = {"per_kstep": float(alpha), "fixed": float(beta)}
     lplan.destroy()
