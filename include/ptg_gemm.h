@@ -247,11 +247,11 @@ typedef enum gemm_sched_mode {
  *                   many workgroups as can be resident at once (occupancy x CUs,
  *                   at most one per unit). Without launch cancel, the slots of
  *                   the full grid beyond the resident ones can only start as the
- *                   workers exit, and then leave again: about 13-17 us per
- *                   launch of 1024 tiles with the per-XCD counters (which probe
- *                   every region before a slot gives up), 2-6 us with one
- *                   counter. The schedule is the same either way (the counters
- *                   decide who takes which unit).
+ *                   workers exit, and then leave again: about 6-7 us per launch
+ *                   of 1024 tiles with the per-XCD counters (each late slot
+ *                   probes every region, then counts itself out). The schedule
+ *                   is the same either way (the counters decide who takes which
+ *                   unit).
  */
 typedef struct gemm_tile_desc {
   int32_t bm, bn, bk;
