@@ -147,22 +147,36 @@ __device__ __forceinline__ int32_t k_rotation_of(const KernelArgs &a, uint32_t i
 // counters, the gate and the count itself, so the next launch that uses this
 // state set (the plan's run after next, or the same launch replayed from a
 // graph) starts from zero without a host-side reset.
+// The count has two levels: a workgroup counts into its group (blockIdx mod
+// kExitGroups, one cache line per group), and the workgroup that completes a
+// group counts the group into exit_count; the one that completes the last
+// group resets everything. (With one counter, the late launch slots of a
+// dynamic run, thousands for small tiles, all hit one address at the end:
+// 8192^3 with 128 x 128 tiles lost ~125 us to it.)
 // Relaxed order is enough: a workgroup's claims are returning atomics whose
 // answers it has waited for, so they are performed before its count goes out;
-// the last workgroup resets only after its own count has come back; and the
-// next launch that reads this state starts after this kernel has ended, which
-// orders everything before it. (An acquire-release count writes back and
+// the resetting workgroup resets only after its own counts have come back; and
+// the next launch that reads this state starts after this kernel has ended,
+// which orders everything before it. (An acquire-release count writes back and
 // invalidates the XCD's whole L2 in every exiting workgroup, which the workers
 // still running on that XCD then pay for: 8192^3 static 750 -> 741 us and
 // dynamic 773 -> 755 us without it.)
 __device__ __forceinline__ void leave_run(const KernelArgs &a) {
-  const uint32_t done = __hip_atomic_fetch_add(&a.ctrl->exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (done + 1u == gridDim.x) {
+  const uint32_t g = blockIdx.x % (uint32_t)kExitGroups;
+  const uint32_t in_group = (gridDim.x - g + (uint32_t)kExitGroups - 1u) / (uint32_t)kExitGroups;
+  const uint32_t groups = min(gridDim.x, (uint32_t)kExitGroups);
+  const uint32_t done =
+      __hip_atomic_fetch_add(&a.ctrl->exit_group[g * kExitStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (done + 1u != in_group) return;
+  const uint32_t groups_done = __hip_atomic_fetch_add(&a.ctrl->exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (groups_done + 1u == groups) {
     __hip_atomic_store(&a.ctrl->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&a.ctrl->gate, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&a.ctrl->error, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int x = 0; x < kXcdRegions; ++x)
       __hip_atomic_store(&a.ctrl->xcd_counter[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int x = 0; x < kExitGroups; ++x)
+      __hip_atomic_store(&a.ctrl->exit_group[x * kExitStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&a.ctrl->exit_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -305,6 +319,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     args.ctrl_next->error = 0u;
     args.ctrl_next->exit_count = 0u;
     for (int x = 0; x < kXcdRegions; ++x) args.ctrl_next->xcd_counter[x] = 0u;
+    for (int x = 0; x < kExitGroups; ++x) args.ctrl_next->exit_group[x * kExitStride] = 0u;
   }
   if (args.clear_count > 0) {
     const uint32_t chunk = ((uint32_t)args.clear_count + gridDim.x - 1u) / gridDim.x;

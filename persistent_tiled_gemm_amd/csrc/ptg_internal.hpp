@@ -28,15 +28,23 @@ static constexpr int kXcdRegions = 8;
 // also leaves its own set's counters at zero (the last workgroup to finish
 // resets them, and the last chunk of a split tile resets its arrival count), so
 // a captured launch replayed again and again on the same set starts clean too.
-struct alignas(64) SchedCtrl {
+// Workgroups count themselves out of a run in kExitGroups groups (workgroup w
+// in group w mod kExitGroups), each group's count on a cache line of its own:
+// thousands of late launch slots leaving at once serialise on one counter.
+static constexpr int kExitGroups = 16;
+static constexpr int kExitStride = 32;  // u32 words from one group's count to the next (128 bytes)
+
+struct alignas(128) SchedCtrl {
   uint32_t counter;    // dynamic claim counter (single-counter policy)
   uint32_t gate;       // workgroups currently holding a concurrency slot
   uint32_t error;      // bit 0: a gate wait ran out; bit 1: ring record for the wrong ordinal
-  uint32_t exit_count; // workgroups of the run that have finished (the last one resets the counters)
+  uint32_t exit_count; // exit groups whose workgroups have all finished (the last group resets the counters)
   uint32_t pad[4];
   uint32_t xcd_counter[kXcdRegions];  // per-XCD claim counters (XCD-partitioned policy)
+  uint32_t pad2[16];
+  uint32_t exit_group[kExitGroups * kExitStride];  // group g's finished workgroups at [g * kExitStride]
 };
-static_assert(sizeof(SchedCtrl) == 64, "control block layout");
+static_assert(sizeof(SchedCtrl) == 128 + 128 * kExitGroups, "control block layout");
 
 // Most tiles one run may split along K (the partial last wave); each has an
 // arrival counter in the scheduler-state set.
