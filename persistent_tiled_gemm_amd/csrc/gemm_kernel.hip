@@ -935,67 +935,61 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     };
 
     if (!split) {
-      if constexpr (CF::MB == 16) {
-        // Whole rows per store. Written straight from the accumulators, one
-        // store covers 16 rows x 64 B (half lines), and a CU then writes its
-        // 256 KiB tile in about 7 us whether or not other CUs store too
-        // (measured with a store-only kernel), while stores of whole rows take
-        // about 2 us alone and reach about 8 TB/s when every CU stores at once.
-        // So each wave passes its WM x WN accumulators through its quarter of
-        // the stage ring, RP rows at a time, and reads them back a row at a
-        // time: each store then writes RPR rows x 512 contiguous bytes. 16-byte
-        // chunk c of row r sits in slot c ^ (r mod 16), which keeps both the
-        // block-shaped writes and the row-shaped reads free of bank conflicts.
-        constexpr int WAVE_LDS = CF::LDS / CF::NW;
-        constexpr int ROW_B = CF::WN * 4;
-        constexpr int RP = WAVE_LDS / ROW_B;
-        constexpr int CHUNKS = ROW_B / 16;
-        constexpr int RPR = 1024 / ROW_B;
-        constexpr int MI_PASS = RP / CF::MB;
-        static_assert(CF::WM % RP == 0 && RP % CF::MB == 0 && CHUNKS * RPR == 64 && CF::QUADS == 1, "epilogue");
-        // every wave's loads into the stages have landed and its fragment reads
-        // are done before any wave overwrites the stages
-        wait_vmem_all();
-        wg_barrier();
-        unsigned char *wl = smem + wave * WAVE_LDS;
+      // Whole rows per store. Written straight from the accumulators, one
+      // store covers 16 rows x 64 B (16 x 16 blocks) or 32 rows x 32 B (32 x
+      // 32 blocks), and a CU then writes a 256 KiB tile in about 7 us whether
+      // or not other CUs store too (measured with a store-only kernel), while
+      // stores of whole rows take about 2 us alone and reach about 8 TB/s when
+      // every CU stores at once. So each wave passes its WM x WN accumulators
+      // through its quarter of the stage ring, RP rows at a time, and reads
+      // them back a row at a time: each store then writes RPR rows of WN
+      // contiguous floats. 16-byte chunk c of row r sits in slot c ^ (r mod 16),
+      // which keeps the block-shaped writes and the row-shaped reads free of
+      // bank conflicts. Lane l holds, in each group of four accumulators, 4
+      // consecutive n of row l mod MB (see the comment above store_group).
+      constexpr int WAVE_LDS = CF::LDS / CF::NW;
+      constexpr int ROW_B = CF::WN * 4;
+      constexpr int RP = WAVE_LDS / ROW_B < CF::WM ? WAVE_LDS / ROW_B : CF::WM;
+      constexpr int CHUNKS = ROW_B / 16;
+      constexpr int RPR = 1024 / ROW_B;
+      constexpr int MI_PASS = RP / CF::MB;
+      static_assert(CF::WM % RP == 0 && RP % CF::MB == 0 && CHUNKS * RPR == 64 && CHUNKS <= 32, "epilogue");
+      // every wave's loads into the stages have landed and its fragment reads
+      // are done before any wave overwrites the stages
+      wait_vmem_all();
+      wg_barrier();
+      unsigned char *wl = smem + wave * WAVE_LDS;
 #pragma unroll
-        for (int p = 0; p < CF::WM / RP; ++p) {
+      for (int p = 0; p < CF::WM / RP; ++p) {
 #pragma unroll
-          for (int mi = p * MI_PASS; mi < (p + 1) * MI_PASS; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < CF::NI; ++ni) {
-              const uint32_t row = (uint32_t)((mi - p * MI_PASS) * CF::MB) + lane % CF::MB;
-              const uint32_t c = (uint32_t)(ni * (CF::MB / 4)) + lane / CF::MB;
-              *(f32x4 *)(wl + row * ROW_B + ((c ^ (row & 15u)) << 4)) =
-                  f32x4{acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]};
-            }
-          // the wave's own LDS writes complete before its reads of other lanes' data
-          wait_lds_all();
-          __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-          for (int i = 0; i < RP / RPR; ++i) {
-            const uint32_t row = (uint32_t)(i * RPR) + lane / CHUNKS;
-            const uint32_t c = lane % CHUNKS;
-            const f32x4 v = *(const f32x4 *)(wl + row * ROW_B + ((c ^ (row & 15u)) << 4));
-            const int32_t m = m0 + (int32_t)(wm * CF::WM + p * RP + row);
-            const int32_t n = n0 + (int32_t)(wn * CF::WN + 4 * c);
-            if (interior || (m < M && n < N)) __builtin_nontemporal_store(v, (f32x4 *)(pb.C + (size_t)m * (size_t)N + n));
-          }
-          // the reads are done before the next pass (or the next unit's loads) writes the region
-          wait_lds_all();
-          __builtin_amdgcn_wave_barrier();
-        }
-        wg_barrier();
-      } else {
-#pragma unroll
-        for (int mi = 0; mi < CF::MI; ++mi)
+        for (int mi = p * MI_PASS; mi < (p + 1) * MI_PASS; ++mi)
 #pragma unroll
           for (int ni = 0; ni < CF::NI; ++ni)
 #pragma unroll
-            for (int qd = 0; qd < CF::QUADS; ++qd)
-              store_group(mi, ni, qd, f32x4{acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1],
-                                            acc[mi][ni][4 * qd + 2], acc[mi][ni][4 * qd + 3]});
+            for (int qd = 0; qd < CF::QUADS; ++qd) {
+              const uint32_t row = (uint32_t)((mi - p * MI_PASS) * CF::MB) + lane % CF::MB;
+              const uint32_t c = (uint32_t)(ni * (CF::MB / 4) + 2 * qd) + lane / CF::MB;
+              *(f32x4 *)(wl + row * ROW_B + ((c ^ (row & 15u)) << 4)) =
+                  f32x4{acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1], acc[mi][ni][4 * qd + 2],
+                        acc[mi][ni][4 * qd + 3]};
+            }
+        // the wave's own LDS writes complete before its reads of other lanes' data
+        wait_lds_all();
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+        for (int i = 0; i < RP / RPR; ++i) {
+          const uint32_t row = (uint32_t)(i * RPR) + lane / CHUNKS;
+          const uint32_t c = lane % CHUNKS;
+          const f32x4 v = *(const f32x4 *)(wl + row * ROW_B + ((c ^ (row & 15u)) << 4));
+          const int32_t m = m0 + (int32_t)(wm * CF::WM + p * RP + row);
+          const int32_t n = n0 + (int32_t)(wn * CF::WN + 4 * c);
+          if (interior || (m < M && n < N)) __builtin_nontemporal_store(v, (f32x4 *)(pb.C + (size_t)m * (size_t)N + n));
+        }
+        // the reads are done before the next pass (or the next unit's loads) writes the region
+        wait_lds_all();
+        __builtin_amdgcn_wave_barrier();
       }
+      wg_barrier();
     } else {
       // K-chunk of a split tile: publish the partial sum; the workgroup that
       // completes the tile's last chunk adds all partials in chunk order and
