@@ -620,7 +620,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     // 16 x 16 main loop places its reads and loads itself.)
     constexpr int kReads = CF::MI + (BT ? 1 : 2) * CF::NI;
     auto read_frags = [&](int st, int s, bf16x8(&af)[CF::MI], bf16x8(&bfr)[CF::NI], int lst, int32_t kt_load,
-                          int count, const uint32_t *voff_fast = nullptr) {
+                          int count, const uint32_t *voff_fast = nullptr, int j0 = 0) {
       const unsigned char *sa = smem + CF::a_off(st);
       const unsigned char *sb = smem + CF::b_off(st);
       i32x4 ra = {0, 0, 0, 0}, rb = {0, 0, 0, 0};
@@ -652,8 +652,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 #pragma unroll
         for (int j = 0; j < count; ++j)
           if (j == r)
-            load16_to_lds(j < CF::A_LOADS ? ra : rb, lbase + load_dst(j, lst),
-                          voff_fast ? voff_fast[j] : load_voff(j, kt_load));
+            load16_to_lds(j0 + j < CF::A_LOADS ? ra : rb, lbase + load_dst(j0 + j, lst),
+                          voff_fast ? voff_fast[j0 + j] : load_voff(j0 + j, kt_load));
       }
     };
 
@@ -691,7 +691,8 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     if constexpr (CF::MB == 32) {
       if (ke > kb) {
         // four 32-deep stages: the loads of k-step kt+3 go out during k-step kt
-        // into the stage k-step kt-1 just left, so a load has three k-steps to land;
+        // into the stage k-step kt-1 just left, so a load has two and a half to
+        // three k-steps to land;
         // each k-step is two 16-deep MFMA slices, and the fragments of one slice
         // are read while the other's MFMAs run
         static_assert(kLoads == 4, "stage ring");
@@ -711,15 +712,18 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         const int32_t slow_from = (K % CF::BK != 0 && full < ke) ? max(kb, full - 3) : ke;
         auto step = [&](int32_t kt, bool fast) {
           const int st = (kt - kb) & 3;
-          read_frags(st, 1, a1, b1, (st + 3) & 3, kt + 3, kLoads, fast ? voff_fast : nullptr);
+          // two of the four loads of k-step kt+3 go out with each slice's reads
+          // (spread over the step: 4096^3 dynamic 175 -> 152 us against all four
+          // with the first slice)
+          read_frags(st, 1, a1, b1, (st + 3) & 3, kt + 3, kLoads / 2, fast ? voff_fast : nullptr);
           mma(a0, b0);
           interleave<kReads, kMfma>();
-          // stage st fully read and stage st+1 landed (its loads went out two k-steps
-          // ago; the eight loads issued since may still be in flight)
+          // stage st fully read and stage st+1 landed (its loads went out during
+          // step kt-2; the six loads issued since may still be in flight)
           wait_lds_all();
-          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+          asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
           wg_barrier();
-          read_frags((st + 1) & 3, 0, a0, b0, 0, 0, 0);
+          read_frags((st + 1) & 3, 0, a0, b0, (st + 3) & 3, kt + 3, kLoads / 2, fast ? voff_fast : nullptr, kLoads / 2);
           mma(a1, b1);
           interleave<kReads, kMfma>();
         };
