@@ -924,84 +924,87 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     }
 
     // ---- epilogue: fp32 accumulators -> C. Lane l holds, in each group of four
-    // accumulators, 4 consecutive n of row m = l % MB: n = 8 qd + 4 (l / 32) for
-    // 32 x 32 blocks, 4 (l / 16) for 16 x 16 blocks. Group g = (mi NI + ni)
-    // QUADS + qd of a thread is its g-th 16-byte store. C is written once and
-    // never read by the kernel, so the stores are non-temporal: they do not
+    // accumulators, 4 consecutive n of row m = l % MB of its block: n = 8 qd +
+    // 4 (l / 32) for 32 x 32 blocks, 4 (l / 16) for 16 x 16 blocks; group g =
+    // (mi NI + ni) QUADS + qd of a thread is its g-th group. C is written once
+    // and never read by the kernel, so the stores are non-temporal: they do not
     // displace the A and B slices the XCD's other workgroups are still reading
     // from L2 (measured 1-3% faster across the modes).
     const bool interior = m0 + BM <= M && n0 + BN <= N;
 
-    auto store_group = [&](int mi, int ni, int qd, const f32x4 &v) {
-      const int32_t m = m0 + (int32_t)(wm * CF::WM + mi * CF::MB + (lane % CF::MB));
-      const int32_t n = n0 + (int32_t)(wn * CF::WN + ni * CF::MB + 8 * qd + 4 * (lane / CF::MB));
-      if (interior || (m < M && n < N)) __builtin_nontemporal_store(v, (f32x4 *)(pb.C + (size_t)m * (size_t)N + n));
-    };
-
-    if (!split) {
-      // Whole rows per store. Written straight from the accumulators, one
-      // store covers 16 rows x 64 B (16 x 16 blocks) or 32 rows x 32 B (32 x
-      // 32 blocks), and a CU then writes a 256 KiB tile in about 7 us whether
-      // or not other CUs store too (measured with a store-only kernel), while
-      // stores of whole rows take about 2 us alone and reach about 8 TB/s when
-      // every CU stores at once. So each wave passes its WM x WN accumulators
-      // through its quarter of the stage ring, RP rows at a time, and reads
-      // them back a row at a time: each store then writes RPR rows of WN
-      // contiguous floats. 16-byte chunk c of row r sits in slot c ^ (r mod 16),
-      // which keeps the block-shaped writes and the row-shaped reads free of
-      // bank conflicts. Lane l holds, in each group of four accumulators, 4
-      // consecutive n of row l mod MB (see the comment above store_group).
-      constexpr int WAVE_LDS = CF::LDS / CF::NW;
-      constexpr int ROW_B = CF::WN * 4;
-      constexpr int RP = WAVE_LDS / ROW_B < CF::WM ? WAVE_LDS / ROW_B : CF::WM;
-      constexpr int CHUNKS = ROW_B / 16;
-      constexpr int RPR = 1024 / ROW_B;
-      constexpr int MI_PASS = RP / CF::MB;
-      static_assert(CF::WM % RP == 0 && RP % CF::MB == 0 && CHUNKS * RPR == 64 && CHUNKS <= 32, "epilogue");
+    // Whole rows per store. Written straight from the accumulators, one store
+    // covers 16 rows x 64 B (16 x 16 blocks) or 32 rows x 32 B (32 x 32
+    // blocks), and a CU then writes a 256 KiB tile in about 7 us whether or not
+    // other CUs store too (measured with a store-only kernel), while stores of
+    // whole rows take about 2 us alone and reach about 8 TB/s when every CU
+    // stores at once. So each wave passes its WM x WN results through its
+    // quarter of the stage ring, RP rows (a pass) at a time, and reads them back
+    // a row at a time: each store then writes RPR rows of WN contiguous floats.
+    // 16-byte chunk c of row r sits in slot c ^ (r mod 16), which keeps the
+    // block-shaped writes and the row-shaped reads free of bank conflicts.
+    // epi_begin / epi_end bracket the use of the ring (every wave calls them);
+    // stage writes a group of four results of pass p, flush stores pass p.
+    constexpr int WAVE_LDS = CF::LDS / CF::NW;
+    constexpr int ROW_B = CF::WN * 4;
+    constexpr int RP = WAVE_LDS / ROW_B < CF::WM ? WAVE_LDS / ROW_B : CF::WM;
+    constexpr int CHUNKS = ROW_B / 16;
+    constexpr int RPR = 1024 / ROW_B;
+    constexpr int MI_PASS = RP / CF::MB;
+    constexpr int PASSES = CF::WM / RP;
+    static_assert(CF::WM % RP == 0 && RP % CF::MB == 0 && CHUNKS * RPR == 64 && CHUNKS <= 32, "epilogue");
+    unsigned char *wl = smem + wave * WAVE_LDS;
+    auto epi_begin = [&]() {
       // every wave's loads into the stages have landed and its fragment reads
       // are done before any wave overwrites the stages
       wait_vmem_all();
       wg_barrier();
-      unsigned char *wl = smem + wave * WAVE_LDS;
+    };
+    auto stage = [&](int p, int mi, int ni, int qd, const f32x4 &v) {
+      const uint32_t row = (uint32_t)((mi - p * MI_PASS) * CF::MB) + lane % CF::MB;
+      const uint32_t c = (uint32_t)(ni * (CF::MB / 4) + 2 * qd) + lane / CF::MB;
+      *(f32x4 *)(wl + row * ROW_B + ((c ^ (row & 15u)) << 4)) = v;
+    };
+    auto flush = [&](int p) {
+      // the wave's own LDS writes complete before its reads of other lanes' data
+      wait_lds_all();
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+      for (int i = 0; i < RP / RPR; ++i) {
+        const uint32_t row = (uint32_t)(i * RPR) + lane / CHUNKS;
+        const uint32_t c = lane % CHUNKS;
+        const f32x4 v = *(const f32x4 *)(wl + row * ROW_B + ((c ^ (row & 15u)) << 4));
+        const int32_t m = m0 + (int32_t)(wm * CF::WM + p * RP + row);
+        const int32_t n = n0 + (int32_t)(wn * CF::WN + 4 * c);
+        if (interior || (m < M && n < N)) __builtin_nontemporal_store(v, (f32x4 *)(pb.C + (size_t)m * (size_t)N + n));
+      }
+      // the reads are done before the next pass (or the next unit's loads) writes the region
+      wait_lds_all();
+      __builtin_amdgcn_wave_barrier();
+    };
+    auto epi_end = [&]() { wg_barrier(); };
+
+    if (!split) {
+      epi_begin();
 #pragma unroll
-      for (int p = 0; p < CF::WM / RP; ++p) {
+      for (int p = 0; p < PASSES; ++p) {
 #pragma unroll
         for (int mi = p * MI_PASS; mi < (p + 1) * MI_PASS; ++mi)
 #pragma unroll
           for (int ni = 0; ni < CF::NI; ++ni)
 #pragma unroll
-            for (int qd = 0; qd < CF::QUADS; ++qd) {
-              const uint32_t row = (uint32_t)((mi - p * MI_PASS) * CF::MB) + lane % CF::MB;
-              const uint32_t c = (uint32_t)(ni * (CF::MB / 4) + 2 * qd) + lane / CF::MB;
-              *(f32x4 *)(wl + row * ROW_B + ((c ^ (row & 15u)) << 4)) =
-                  f32x4{acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1], acc[mi][ni][4 * qd + 2],
-                        acc[mi][ni][4 * qd + 3]};
-            }
-        // the wave's own LDS writes complete before its reads of other lanes' data
-        wait_lds_all();
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-        for (int i = 0; i < RP / RPR; ++i) {
-          const uint32_t row = (uint32_t)(i * RPR) + lane / CHUNKS;
-          const uint32_t c = lane % CHUNKS;
-          const f32x4 v = *(const f32x4 *)(wl + row * ROW_B + ((c ^ (row & 15u)) << 4));
-          const int32_t m = m0 + (int32_t)(wm * CF::WM + p * RP + row);
-          const int32_t n = n0 + (int32_t)(wn * CF::WN + 4 * c);
-          if (interior || (m < M && n < N)) __builtin_nontemporal_store(v, (f32x4 *)(pb.C + (size_t)m * (size_t)N + n));
-        }
-        // the reads are done before the next pass (or the next unit's loads) writes the region
-        wait_lds_all();
-        __builtin_amdgcn_wave_barrier();
+            for (int qd = 0; qd < CF::QUADS; ++qd)
+              stage(p, mi, ni, qd, f32x4{acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1], acc[mi][ni][4 * qd + 2],
+                                         acc[mi][ni][4 * qd + 3]});
+        flush(p);
       }
-      wg_barrier();
+      epi_end();
     } else {
       // K-chunk of a split tile: publish the partial sum; the workgroup that
       // completes the tile's last chunk adds all partials in chunk order and
       // writes C. The order is fixed, so the result does not depend on who
       // finished last. Partial slots are thread-major per 16-byte group: fully
-      // coalesced. The sum reads the slots (this workgroup's own partial
-      // included) in batches of up to 16 groups per thread, all of a chunk's
-      // loads of a batch in flight at once; the accumulators are not touched.
+      // coalesced. The sum reads the other chunks' slots in batches of up to
+      // 16 groups per thread, all of a chunk's loads of a batch in flight at once.
       const uint32_t S = (uint32_t)args.split_chunks;
       const uint32_t q = tile - (uint32_t)args.split_base;
       f32x4 *slot = reinterpret_cast<f32x4 *>(args.ws) + (size_t)(item - (uint32_t)args.split_base) * (BM * BN / 4);
@@ -1026,30 +1029,37 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       __syncthreads();
       if (wave_uniform(split_last) != 0) {
         __threadfence();  // acquire the other chunks' partials
+        // the sum in chunk order, staged straight into the ring a pass at a
+        // time and stored in whole rows like a whole tile
         const f32x4 *base = reinterpret_cast<const f32x4 *>(args.ws) + (size_t)q * S * (BM * BN / 4) + tid;
-        constexpr int kGroups = CF::MI * CF::NI * CF::QUADS;
-        constexpr int kBatch = kGroups < 16 ? kGroups : 16;
-        static_assert(kGroups % kBatch == 0, "batches");
-        for (int g0 = 0; g0 < kGroups; g0 += kBatch) {
-          f32x4 v[kBatch];
+        constexpr int kPassGroups = MI_PASS * CF::NI * CF::QUADS;  // groups g of pass p: p kPassGroups + [0, kPassGroups)
+        constexpr int kBatch = kPassGroups < 16 ? kPassGroups : 16;
+        static_assert(kPassGroups % kBatch == 0, "batches");
+        epi_begin();
+        for (int p = 0; p < PASSES; ++p) {
+          for (int g0 = p * kPassGroups; g0 < (p + 1) * kPassGroups; g0 += kBatch) {
+            f32x4 v[kBatch];
 #pragma unroll
-          for (int i = 0; i < kBatch; ++i) v[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-          for (uint32_t c = 0; c < S; ++c) {
-            const f32x4 *src = base + (size_t)c * (BM * BN / 4) + (size_t)g0 * CF::THREADS;
-            f32x4 p[kBatch];
+            for (int i = 0; i < kBatch; ++i) v[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (uint32_t c = 0; c < S; ++c) {
+              const f32x4 *src = base + (size_t)c * (BM * BN / 4) + (size_t)g0 * CF::THREADS;
+              f32x4 part[kBatch];
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i) p[i] = src[(size_t)i * CF::THREADS];
+              for (int i = 0; i < kBatch; ++i) part[i] = src[(size_t)i * CF::THREADS];
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i)
+              for (int i = 0; i < kBatch; ++i)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[i][e] += p[i][e];
+                for (int e = 0; e < 4; ++e) v[i][e] += part[i][e];
+            }
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+              const int g = g0 + i;
+              stage(p, g / (CF::NI * CF::QUADS), (g / CF::QUADS) % CF::NI, g % CF::QUADS, v[i]);
+            }
           }
-#pragma unroll
-          for (int i = 0; i < kBatch; ++i) {
-            const int g = g0 + i;
-            store_group(g / (CF::NI * CF::QUADS), (g / CF::QUADS) % CF::NI, g % CF::QUADS, v[i]);
-          }
+          flush(p);
         }
+        epi_end();
       }
     }
 
