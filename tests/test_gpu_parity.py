@@ -14,6 +14,7 @@ import pytest
 import persistent_tiled_gemm_amd as ptg
 from tests.gpu_util import (assert_close_full, check_log, make_plan, new_c, run, say, torch_mod, upload)
 from workloads import f32_to_bf16_bits, make_problem
+from oracle.gemm_ref import gemm_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -305,4 +306,61 @@ def test_python_gemm_entry():
         ptg.gemm(A.float(), B)                  # wrong dtype
     with pytest.raises(ValueError):
         ptg.gemm(A, B[:, :200])                  # not contiguous
+    plan.destroy()
+
+
+def _bits(rng, shape, exp, signed=True):
+    """bf16 bit patterns with biased exponent field `exp` (0: subnormal) and random 7-bit mantissas
+    (never zero for subnormals) and, when `signed`, random signs."""
+    man = rng.integers(1 if exp == 0 else 0, 128, size=shape)
+    sign = rng.integers(0, 2, size=shape) << 15 if signed else 0
+    return ((exp << 7) | man | sign).astype(np.uint16)
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+def test_subnormal_and_nonfinite_inputs(tile):
+    """bf16 subnormal operands take part at full value (no flush to zero), fp32-subnormal
+    products keep the fp32 subnormal spacing, and Inf / NaN / overflow come out as the
+    rounded fp64 result says: IEEE products and sums rounded to fp32."""
+    from workloads import GemmProblem
+    rng = np.random.default_rng(21)
+    M, N, K = 300, 264, 200
+    plan = make_plan(tile)
+    big = 127 + 100  # 2^100: subnormal x big lands in the normal fp32 range
+    cases = {
+        "subnormal A": GemmProblem(_bits(rng, (M, K), 0), _bits(rng, (K, N), big)),
+        "subnormal B": GemmProblem(_bits(rng, (M, K), big), _bits(rng, (K, N), 0)),
+    }
+    for mode in MODES:
+        for name, p in cases.items():
+            say(f"case {name} tile={tile} mode={mode}")
+            assert_close_full(p, run(p, plan, mode))
+        # products near 2^-140: below the fp32 normal range; each rounding is to the subnormal spacing 2^-149
+        say(f"case fp32-subnormal products tile={tile} mode={mode}")
+        p = GemmProblem(_bits(rng, (M, K), 127 - 70), _bits(rng, (K, N), 127 - 70))
+        c = run(p, plan, mode).astype(np.float64)
+        ref = gemm_ref(p.a_bits, p.b_bits)
+        assert np.abs(c - ref).max() <= K * 2.0 ** -149
+        assert np.linalg.norm(c - ref) <= 1e-3 * np.linalg.norm(ref)
+        # Inf, -Inf and NaN in A; a zero in B meets A's +Inf (Inf x 0 = NaN)
+        say(f"case non-finite tile={tile} mode={mode}")
+        a = _bits(rng, (M, K), 127, signed=False)
+        b = _bits(rng, (K, N), 127)
+        a[3, 17], a[290, 199], a[20, 5] = 0x7F80, 0xFF80, 0x7FC0
+        b[17, 11] = 0x0000
+        p = GemmProblem(a, b)
+        c = run(p, plan, mode).astype(np.float64)
+        with np.errstate(invalid="ignore"):
+            ref = gemm_ref(a, b)
+        for pred in (np.isnan, np.isposinf, np.isneginf):
+            assert np.array_equal(pred(c), pred(ref)), pred.__name__
+        assert np.isnan(c[20]).all() and np.isnan(c[3, 11]) and np.isinf(c[290]).all()
+        fin = np.isfinite(ref)
+        bound = 1e-2 * np.sqrt(K) * 2.0 * 2.0 * 2.0 ** -8
+        assert np.abs(c[fin] - ref[fin]).max() <= bound
+        # |exact| above the fp32 range rounds to Inf
+        say(f"case overflow tile={tile} mode={mode}")
+        p = GemmProblem(_bits(rng, (M, K), 127 + 70, signed=False), _bits(rng, (K, N), 127 + 70, signed=False))
+        c = run(p, plan, mode)
+        assert np.isposinf(c).all()
     plan.destroy()
