@@ -124,15 +124,29 @@ __device__ __forceinline__ void decode_tile(int32_t t, int32_t tiles_m, int32_t 
   n_t = r / gm;
 }
 
-// Which entry of a grouped launch's table owns work unit u (unit_start ascending:
-// the table is in claim order).
+// Which entry of a grouped launch's table owns work unit u: the last entry
+// whose unit_start is <= u. unit_start ascends (the table is in claim order;
+// an entry with no units shares its unit_start with the next one), so the
+// entries with unit_start <= u are a prefix of the table and the answer is
+// their count less one. Called by whole waves with a wave-uniform u: lane l
+// tests entries l, l + 64, ..., four loads at a time. The loads are
+// independent, so a table of up to 256 entries costs one load round trip (a
+// binary search costs log2 G dependent ones: on 64 problems, about 5 us of a
+// 600 us launch).
 __device__ __forceinline__ int32_t find_problem(const KernelProblem *probs, int32_t G, int32_t u) {
-  int32_t lo = 0, hi = G - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (probs[mid].unit_start <= u) lo = mid; else hi = mid - 1;
+  const int32_t lane = (int32_t)(threadIdx.x & 63u);
+  int32_t count = 0;
+  for (int32_t base = 0; base < G; base += 256) {
+    int32_t us[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int32_t i = base + 64 * q + lane;
+      us[q] = probs[i < G ? i : 0].unit_start;  // lanes past the end reload entry 0
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) count += __popcll(__ballot(base + 64 * q + lane < G && us[q] <= u));
   }
-  return lo;
+  return count - 1;
 }
 
 }  // namespace ptg

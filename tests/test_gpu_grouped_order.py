@@ -124,3 +124,37 @@ def test_contiguous_regions_small_ragged_problems():
         log = check_log(plan, "dynamic", T, K=_tile_k(problems, 256))
         assert log["tile"].tolist() == want
         plan.destroy()
+
+
+@pytest.mark.parametrize("G", [300, 1100])
+@pytest.mark.parametrize("order,policy", [(0, 1), (1, 1), (1, 2)])
+def test_many_problems_with_empty_ones(G, order, policy):
+    """More problems than one round of the kernel's problem lookup covers (256
+    table entries), some of them with no tiles (M or N zero, sharing their first
+    unit with the next problem): every unit must find its own problem, in the
+    given order, longest K first, and dealt to contiguous regions."""
+    rng = np.random.default_rng(G + 10 * order + policy)
+    shapes = [(int(rng.choice([0, 1, 40, 136, 264, 300])), int(rng.choice([0, 8, 136, 264])),
+               int(rng.choice([8, 64, 136]))) for _ in range(G)]
+    problems = [make_problem(M, N, K, "uniform", seed=1000 + i) for i, (M, N, K) in enumerate(shapes)]
+    tiles = [-(-M // 256) * -(-N // 256) for M, N, _ in shapes]
+    ks = [K for _, _, K in shapes]
+    T = sum(tiles)
+    assert sum(1 for t in tiles if t == 0) > G // 4 and T > 256
+    if order == 0:
+        want = list(range(T))
+    elif policy == 2:
+        want = _dealt_order(ks, tiles)
+    else:
+        want = lpt_claim_order(ks, tiles)
+    plan = make_plan(256, group_order=order, claim_policy=policy, max_groups=2048)
+    for mode in MODES:
+        say(f"case many problems G={G} T={T} group_order={order} claim_policy={policy} mode={mode}")
+        cs = _run_grouped(problems, plan, mode)
+        for q, c in zip(problems, cs):
+            if q.M and q.N:
+                assert_close_full(q, c)
+        info = ptg.gemm_plan_info_get(plan)
+        log = check_log(plan, mode, T, P=info["last_grid"] if mode == "static" else None, K=_tile_k(problems, 256))
+        assert log["tile"].tolist() == want
+    plan.destroy()
