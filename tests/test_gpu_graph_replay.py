@@ -91,3 +91,44 @@ def test_split_tail_replayed_from_a_graph():
     say("case graph replay split tail")
     _replay_and_check(lambda s: ptg.gemm_run(A, B, C, plan, mode="dynamic", stream=s), C, eager)
     plan.destroy()
+
+
+@pytest.mark.parametrize("mode,order,policy", [("static", 0, 1), ("dynamic", 0, 1), ("dynamic", 1, 2)])
+def test_grouped_run_replayed_from_a_graph(mode, order, policy):
+    # the problem table was uploaded by the eager run and is unchanged, so the
+    # captured call holds the kernel only; every replay must match the eager run
+    torch = torch_mod()
+    shapes = [(300, 264, 520), (0, 64, 64), (700, 256, 64), (256, 136, 1000), (1, 8, 8), (513, 704, 96)]
+    problems = [make_problem(M, N, K, "uniform", seed=90 + i) for i, (M, N, K) in enumerate(shapes)]
+    As = [ptg.bf16_from_bits(q.a_bits) for q in problems]
+    Bs = [ptg.bf16_from_bits(q.b_bits) for q in problems]
+    Cs = [torch.full((q.M, q.N), float("nan"), dtype=torch.float32, device="cuda") for q in problems]
+    plan = ptg.gemm_create(tile_edge=256, group_order=order, claim_policy=policy)
+    ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode)
+    ptg.gemm_sync(plan)
+    eager = [c.clone() for c in Cs]
+    for q, c in zip(problems, eager):
+        if q.M:
+            assert_close_rows(q, c.cpu().numpy(), [0, q.M - 1])
+    say(f"case graph replay grouped mode={mode} group_order={order} claim_policy={policy}")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode, stream=s)
+    s.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        ptg.gemm_run_grouped(As, Bs, Cs, plan, mode=mode, stream=s)
+    other = torch.randn(512, 512, device="cuda")
+    for i in range(4):
+        for c in Cs:
+            c.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (c, e) in enumerate(zip(Cs, eager)):
+            assert torch.equal(c, e), f"replay {i}: problem {j} differs from the eager run"
+        other = other @ other.T / 512.0
+        torch.cuda.synchronize()
+    del g
+    assert ptg.gemm_sync(plan, strict=False) == 0
+    plan.destroy()
