@@ -185,9 +185,12 @@ typedef enum gemm_sched_mode {
  *   device          HIP device ordinal; must be gfx950.
  *   tail_split      0 = off. s in 2..GEMM_MAX_TAIL_SPLIT: split each tile of a
  *                   partial last wave into at most s K-chunks (fewer when the
- *                   idle workers or K, at >= 4 k-steps a chunk, allow fewer).
- *                   Workers per wave: the static mode's P, else occupancy x
- *                   CUs. gemm_create then reserves the partial-sum scratch:
+ *                   idle workers or K, at >= 8 k-steps of bk a chunk, allow
+ *                   fewer). Workers per wave: the static mode's P, else
+ *                   occupancy x CUs. A run with fewer tiles than that is one
+ *                   partial wave, so all its tiles split (on MI355X, 2048 x
+ *                   2048 x 8192 with 256 x 256 tiles: 64 tiles, 4 chunks each).
+ *                   gemm_create then reserves the partial-sum scratch:
  *                   bm x bn x 4 bytes per worker of one wave.
  *   group_order     grouped runs only: the order work units are handed out in.
  *                   0 = problem after problem, as given. 1 = problems with the

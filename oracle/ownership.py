@@ -185,10 +185,11 @@ def split_units(T: int, workers: int, nk: int, max_chunks: int, min_chunk_steps:
     r = T mod workers tiles of the partial last wave is cut into
     S = min(max_chunks, workers // r, nk // min_chunk_steps) K-chunks when S >= 2,
     chunk c covering k-steps [floor(c nk / S), floor((c+1) nk / S)). Units of the
-    split tiles follow the whole ones, tile-major.
+    split tiles follow the whole ones, tile-major. With T < workers the run is a
+    single partial wave, and all T tiles are split.
     """
     whole = [(t, 0, nk) for t in range(T)]
-    if max_chunks < 2 or workers < 2 or T < workers:
+    if max_chunks < 2 or workers < 2 or T == 0:
         return whole
     r = T % workers
     if r == 0 or r > max_split_tiles:

@@ -189,7 +189,8 @@ constexpr int64_t kMinChunkSteps = 8;
 // Work items of a run: T whole tiles, or, with tail splitting on, the tiles
 // that fill whole waves of `workers` plus the r = T mod workers tiles of the
 // partial last wave, each split into S K-chunks (S <= tail_split, <= workers / r
-// so the chunks fit the idle workers, and >= kMinChunkSteps k-steps each).
+// so the chunks fit the idle workers, and >= kMinChunkSteps k-steps each). A
+// run with fewer tiles than workers is one partial wave: all its tiles split.
 // Work units (what one claim, static step or non-persistent block takes) are
 // the items, or with claim groups g consecutive tiles (nothing is then split).
 void plan_units(const gemm_plan *p, bool grouped, int32_t mode, int64_t tiles, int64_t K, int64_t *items,
@@ -205,7 +206,7 @@ void plan_units(const gemm_plan *p, bool grouped, int32_t mode, int64_t tiles, i
   if (grouped || p->desc.tail_split < 2 || p->ws_tiles == 0) return;
   const int64_t workers =
       mode == GEMM_SCHED_STATIC ? (int64_t)p->static_workers : (int64_t)p->occupancy * p->cu_count;
-  if (workers < 2 || tiles < workers) return;
+  if (workers < 2) return;
   const int64_t r = tiles % workers;
   if (r == 0 || r > ptg::kMaxSplitTiles) return;
   const int64_t nk = ceil_div(K, p->desc.bk);

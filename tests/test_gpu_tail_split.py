@@ -141,3 +141,32 @@ def test_tail_split_with_claim_options(tile, q, policy):
     rows = _split_rows(want, tile, M, 1) + [0, tile, M // 2]
     assert_close_rows(p, c, rows)
     plan.destroy()
+
+
+@pytest.mark.parametrize("tile,shape", [(256, (2048, 2048, 8192)), (256, (700, 520, 1000)), (128, (1000, 776, 2056))])
+def test_tail_split_underfilled_grid(tile, shape):
+    """Fewer tiles than workers: the run is a single partial wave and every tile is split
+    (K not a multiple of 32 in the ragged cases: the last chunk holds the partial k-step)."""
+    M, N, K = shape
+    p = make_problem(M, N, K, "normal" if K == 8192 else "uniform", seed=M + K)
+    plan = make_plan(tile, tail_split=4, log_capacity=4096)
+    info = ptg.gemm_plan_info_get(plan)
+    workers = info["occupancy"] * info["cu_count"]
+    tn = -(-N // tile)
+    T = -(-M // tile) * tn
+    assert T < workers
+    rows = sorted(set(range(0, M, 7)) | {M - 1})
+    outs = {}
+    for mode in MODES:
+        say(f"case tail split under-filled tile={tile} shape={shape} mode={mode}")
+        c = run(p, plan, mode)
+        info = ptg.gemm_plan_info_get(plan)
+        S = info["last_split_chunks"]
+        assert S >= 2 and info["last_tiles"] == T and info["last_items"] == T * S, info
+        log = check_log(plan, mode, T * S, P=info["last_grid"] if mode == "static" else None, K=K, tiles=T)
+        _expect_units(plan, log, T, workers, K, 4)
+        assert_close_rows(p, c, rows)
+        outs[mode] = c
+    assert np.array_equal(outs["static"], outs["dynamic"])
+    assert np.array_equal(outs["nonpersistent"], outs["dynamic"])
+    plan.destroy()

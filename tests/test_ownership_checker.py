@@ -118,10 +118,16 @@ def test_split_units_decomposition():
     assert len(split_units(356, 256, 64, 8)) == 256 + 100 * 2
     assert len(split_units(257, 256, 12, 8)) == 256 + 3          # nk // 4 = 3
     assert split_units(257, 256, 7, 8) == [(t, 0, 7) for t in range(257)]   # one chunk only: no split
-    # no partial wave, fewer tiles than workers, splitting off
+    # no partial wave, splitting off
     assert split_units(512, 256, 64, 8) == [(t, 0, 64) for t in range(512)]
-    assert split_units(100, 256, 64, 8) == [(t, 0, 64) for t in range(100)]
     assert split_units(257, 256, 64, 0) == [(t, 0, 64) for t in range(257)]
+    # fewer tiles than workers: the one wave is partial and every tile splits
+    # (100 tiles: 256 // 100 = 2 chunks; 64 tiles: 4 chunks fill all 256 workers)
+    u = split_units(100, 256, 64, 8)
+    assert u == [(t, 32 * c, 32 * c + 32) for t in range(100) for c in range(2)]
+    assert len(split_units(64, 256, 64, 8)) == 256
+    assert split_units(1, 256, 64, 8) == [(0, 8 * c, 8 * c + 8) for c in range(8)]
+    assert split_units(0, 256, 64, 8) == []
     # uneven division of the k-steps still covers [0, nk) exactly
     for T, P, nk, s in ((257, 256, 30, 7), (14, 5, 13, 3), (1030, 256, 100, 64)):
         u = split_units(T, P, nk, s)
