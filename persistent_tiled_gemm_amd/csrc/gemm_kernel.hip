@@ -1005,9 +1005,17 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       // finished last. Partial slots are thread-major per 16-byte group: fully
       // coalesced. The sum reads the other chunks' slots in batches of up to
       // 16 groups per thread, all of a chunk's loads of a batch in flight at once.
+      // The partials are written and read with agent-scope cache policy
+      // (store16_agent / load16_agent): the stores go through to memory and a
+      // vmcnt(0) wait completes them before the arrival count goes out, so the
+      // count itself can be relaxed. Release and acquire fences in their place
+      // write back and invalidate the whole L2 of the XCD; with every tile of a
+      // run split (fewer tiles than workers) they cost 2048 x 2048 x 8192 about
+      // a third of its time.
       const uint32_t S = (uint32_t)args.split_chunks;
       const uint32_t q = tile - (uint32_t)args.split_base;
-      f32x4 *slot = reinterpret_cast<f32x4 *>(args.ws) + (size_t)(item - (uint32_t)args.split_base) * (BM * BN / 4);
+      const __amdgpu_buffer_rsrc_t wsr = make_rsrc(args.ws);
+      const uint32_t slot_off = (item - (uint32_t)args.split_base) * (uint32_t)(BM * BN * 4);
 #pragma unroll
       for (int mi = 0; mi < CF::MI; ++mi)
 #pragma unroll
@@ -1015,23 +1023,24 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 #pragma unroll
           for (int qd = 0; qd < CF::QUADS; ++qd) {
             const int g = (mi * CF::NI + ni) * CF::QUADS + qd;
-            slot[g * CF::THREADS + tid] = f32x4{acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1],
-                                                acc[mi][ni][4 * qd + 2], acc[mi][ni][4 * qd + 3]};
+            store16_agent(wsr, slot_off + (uint32_t)(g * CF::THREADS + (int)tid) * 16u,
+                          f32x4{acc[mi][ni][4 * qd + 0], acc[mi][ni][4 * qd + 1], acc[mi][ni][4 * qd + 2],
+                                acc[mi][ni][4 * qd + 3]});
           }
-      __threadfence();  // release this thread's partial at device scope
+      wait_vmem_all();  // this thread's partial has reached memory
       __syncthreads();
       if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&args.arrivals[q], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t prev = __hip_atomic_fetch_add(&args.arrivals[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         split_last = prev + 1u == S ? 1u : 0u;
         // every chunk has arrived: the count is done with for this run
         if (prev + 1u == S) __hip_atomic_store(&args.arrivals[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
       if (wave_uniform(split_last) != 0) {
-        __threadfence();  // acquire the other chunks' partials
         // the sum in chunk order, staged straight into the ring a pass at a
-        // time and stored in whole rows like a whole tile
-        const f32x4 *base = reinterpret_cast<const f32x4 *>(args.ws) + (size_t)q * S * (BM * BN / 4) + tid;
+        // time and stored in whole rows like a whole tile (the partial loads
+        // go out after the count's answer, which every thread has waited for)
+        const uint32_t base = q * S * (uint32_t)(BM * BN * 4) + tid * 16u;
         constexpr int kPassGroups = MI_PASS * CF::NI * CF::QUADS;  // groups g of pass p: p kPassGroups + [0, kPassGroups)
         constexpr int kBatch = kPassGroups < 16 ? kPassGroups : 16;
         static_assert(kPassGroups % kBatch == 0, "batches");
@@ -1042,10 +1051,10 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
 #pragma unroll
             for (int i = 0; i < kBatch; ++i) v[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             for (uint32_t c = 0; c < S; ++c) {
-              const f32x4 *src = base + (size_t)c * (BM * BN / 4) + (size_t)g0 * CF::THREADS;
+              const uint32_t src = base + c * (uint32_t)(BM * BN * 4) + (uint32_t)(g0 * CF::THREADS) * 16u;
               f32x4 part[kBatch];
 #pragma unroll
-              for (int i = 0; i < kBatch; ++i) part[i] = src[(size_t)i * CF::THREADS];
+              for (int i = 0; i < kBatch; ++i) part[i] = load16_agent(wsr, src + (uint32_t)(i * CF::THREADS) * 16u);
 #pragma unroll
               for (int i = 0; i < kBatch; ++i)
 #pragma unroll

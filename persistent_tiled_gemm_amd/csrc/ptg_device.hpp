@@ -50,6 +50,23 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void *base, bool live) {
   return r;
 }
 
+// 16-byte accesses for data that a workgroup on another XCD reads later in
+// the same run (the split tail's partial sums). The sc1 cache-policy bit (bit
+// 4 of the buffer builtins' policy operand on gfx950) is what the compiler
+// puts on agent-scope atomic loads and stores: the store writes through this
+// XCD's L2 and the load fetches past the reader's. With every access to that
+// data made this way, waiting for the stores (vmcnt(0)) orders them before a
+// later atomic, so no fence is needed; a device-scope fence would write back
+// and invalidate the whole L2 of the XCD, which costs the other workgroups on
+// it their cached operands.
+static constexpr int kPolicyAgent = 16;
+__device__ __forceinline__ void store16_agent(__amdgpu_buffer_rsrc_t r, uint32_t offset, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)offset, 0, kPolicyAgent);
+}
+__device__ __forceinline__ f32x4 load16_agent(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, kPolicyAgent));
+}
+
 template <typename T>
 __device__ __forceinline__ T *uniform_ptr(T *p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
