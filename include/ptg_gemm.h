@@ -189,7 +189,10 @@ typedef enum gemm_sched_mode {
  *                   fewer). Workers per wave: the static mode's P, else
  *                   occupancy x CUs. A run with fewer tiles than that is one
  *                   partial wave, so all its tiles split (on MI355X, 2048 x
- *                   2048 x 8192 with 256 x 256 tiles: 64 tiles, 4 chunks each).
+ *                   2048 x 8192 with 256 x 256 tiles: 64 tiles, 4 chunks each,
+ *                   140 -> 98 us). Off by default: with few k-steps a chunk
+ *                   (K of 2048 or less) or with 128 x 128 tiles and as many
+ *                   tiles as CUs, the partial sums cost more than they save.
  *                   gemm_create then reserves the partial-sum scratch:
  *                   bm x bn x 4 bytes per worker of one wave.
  *   group_order     grouped runs only: the order work units are handed out in.
