@@ -66,15 +66,19 @@
  * which use it. A plan is not thread-safe.
  *
  * Graph capture. gemm_run and gemm_run_noalloc enqueue one kernel and nothing
- * else, and every run leaves the scheduler state it used (claim counters, gate,
- * split-tile arrival counts) back at zero when it ends, so a captured launch
- * can be replayed any number of times. Make a plan's first run on the capture
- * stream before capturing (a run on a new stream first waits for the plan's
- * previous stream with an event), and gemm_run_noalloc's first call on a
- * device outside capture (it clears its state array then). With the tile log
- * on, a replayed launch adds to the visit counts of the previous replay (the
- * log is reset by the plan's next uncaptured run). Grouped runs upload their
- * problem table and are not meant for capture.
+ * else. A gemm_run made while its stream is capturing (hipStreamIsCapturing)
+ * runs on a scheduler-state set of its own and leaves that state (claim
+ * counters, gate, split-tile arrival counts) back at zero when it ends, so the
+ * captured launch can be replayed any number of times; an uncaptured run skips
+ * that clean-up, since the plan's next run clears the set it used (the clean-up
+ * costs 2-4 us at the end of a launch). gemm_run_noalloc always cleans up after
+ * itself. Make a plan's first run on the capture stream before capturing (a run
+ * on a new stream first waits for the plan's previous stream with an event),
+ * and gemm_run_noalloc's first call on a device outside capture (it clears its
+ * state array then). With the tile log on, the visit counts of a captured
+ * launch add up over its replays. A grouped run captures like a single one when
+ * its problem table is the one the plan uploaded last (then it enqueues no
+ * upload).
  *
  * Errors. Every call returns a gemm_status; 0 is success. Invalid arguments are
  * rejected before anything is enqueued. HIP failures return GEMM_E_HIP and the

@@ -47,7 +47,8 @@ struct gemm_plan {
   float *d_ws = nullptr;
   int64_t ws_tiles = 0;  // BM x BN fp32 partial slots in d_ws
   size_t ctrl_set_bytes = 0;
-  uint64_t runs = 0;  // launches so far; run i uses set i % 2
+  uint64_t runs = 0;  // uncaptured launches so far; run i uses set i % 2
+  unsigned char *last_set = nullptr;  // the state set of the last launch (its visit counters)
   TileRecDev *d_log = nullptr;
   KernelProblem *d_groups = nullptr;
   KernelProblem *h_groups = nullptr;  // pinned staging for the grouped table
@@ -144,6 +145,9 @@ gemm_status take_device_status(gemm_plan *p) {
 }
 
 unsigned char *ctrl_set(gemm_plan *p, uint64_t run) { return p->d_ctrl_block + (run & 1u) * p->ctrl_set_bytes; }
+// The set of launches captured into a graph: never cleared by another run, so
+// those launches clean it up themselves (self_clean) for the next replay.
+unsigned char *graph_set(gemm_plan *p) { return p->d_ctrl_block + 2 * p->ctrl_set_bytes; }
 constexpr size_t kArrivalsOffset = sizeof(SchedCtrl);
 constexpr size_t kVisitsOffset = sizeof(SchedCtrl) + sizeof(uint32_t) * (size_t)ptg::kMaxSplitTiles;
 
@@ -259,17 +263,34 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   }
   args.status = p->d_status;
   args.log_cap = p->desc.log_capacity;
-  unsigned char *cur = ctrl_set(p, p->runs), *nxt = ctrl_set(p, p->runs + 1);
+  // An uncaptured run uses set runs % 2 and clears the other for the next run;
+  // a launch being captured into a graph uses the graph set, clears nothing
+  // and leaves its set at zero itself, so that every replay starts clean.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &capture);
+  if (e != hipSuccess) return hip_fail(p, e, "hipStreamIsCapturing");
+  const bool captured = capture != hipStreamCaptureStatusNone;
+  unsigned char *cur = captured ? graph_set(p) : ctrl_set(p, p->runs);
   args.ctrl = reinterpret_cast<SchedCtrl *>(cur);
   args.arrivals = reinterpret_cast<uint32_t *>(cur + kArrivalsOffset);
   args.visits = reinterpret_cast<uint32_t *>(cur + kVisitsOffset);
-  args.ctrl_next = reinterpret_cast<SchedCtrl *>(nxt);
-  args.clear_next = reinterpret_cast<uint32_t *>(nxt + kArrivalsOffset);
-  args.clear_count = ptg::kMaxSplitTiles + p->desc.log_capacity;
+  if (captured) {
+    args.ctrl_next = nullptr;
+    args.clear_next = nullptr;
+    args.clear_count = 0;
+    args.self_clean = 1;
+  } else {
+    unsigned char *nxt = ctrl_set(p, p->runs + 1);
+    args.ctrl_next = reinterpret_cast<SchedCtrl *>(nxt);
+    args.clear_next = reinterpret_cast<uint32_t *>(nxt + kArrivalsOffset);
+    args.clear_count = ptg::kMaxSplitTiles + p->desc.log_capacity;
+    args.self_clean = 0;
+  }
   args.log = p->d_log;
-  hipError_t e = ptg::launch_gemm(p->desc.bm, mode, grouped, p->desc.b_layout == 1, args, (int)grid, p->dyn_lds, s);
+  e = ptg::launch_gemm(p->desc.bm, mode, grouped, p->desc.b_layout == 1, args, (int)grid, p->dyn_lds, s);
   if (e != hipSuccess) return hip_fail(p, e, "kernel launch");
-  ++p->runs;
+  if (!captured) ++p->runs;
+  p->last_set = cur;
   p->last_stream = s;
   p->has_run = true;
   p->last_tiles = tiles;
@@ -440,12 +461,12 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   p->static_workers = d.static_workers > 0 ? d.static_workers : occ * p->cu_count;
 
   p->ctrl_set_bytes = (kVisitsOffset + sizeof(uint32_t) * (size_t)std::max(d.log_capacity, 1) + 255) & ~(size_t)255;
-  if (hipMalloc(&p->d_ctrl_block, 2 * p->ctrl_set_bytes + 256) != hipSuccess) {
+  if (hipMalloc(&p->d_ctrl_block, 3 * p->ctrl_set_bytes + 256) != hipSuccess) {
     delete p;
     return GEMM_E_NOMEM;
   }
-  p->d_status = reinterpret_cast<uint32_t *>(p->d_ctrl_block + 2 * p->ctrl_set_bytes);
-  if (hipMemset(p->d_ctrl_block, 0, 2 * p->ctrl_set_bytes + 256) != hipSuccess) {
+  p->d_status = reinterpret_cast<uint32_t *>(p->d_ctrl_block + 3 * p->ctrl_set_bytes);
+  if (hipMemset(p->d_ctrl_block, 0, 3 * p->ctrl_set_bytes + 256) != hipSuccess) {
     gemm_destroy(p);
     return GEMM_E_HIP;
   }
@@ -579,6 +600,7 @@ gemm_status gemm_run_noalloc(const void *A, const void *B, float *C, int64_t M, 
   args.ctrl_next = reinterpret_cast<SchedCtrl *>(nxt);
   args.clear_next = nullptr;
   args.clear_count = 0;
+  args.self_clean = 1;  // callers capture it into graphs: every run leaves its set at zero
   args.status = d_status ? d_status : reinterpret_cast<uint32_t *>(d->ptr + 2 * kNoallocSetBytes);
   hipError_t e = ptg::launch_gemm(256, sched_mode, false, false, args, (int)grid, 0, s);
   if (e != hipSuccess) return GEMM_E_HIP;
@@ -696,7 +718,7 @@ gemm_status gemm_read_log(gemm_tile_cfg tile_cfg, gemm_tile_rec *host_out, size_
   if (m > 0) {
     e = hipMemcpy(recs.data(), p->d_log, sizeof(TileRecDev) * m, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(log)");
-    e = hipMemcpy(visits.data(), ctrl_set(p, p->runs - 1) + kVisitsOffset, sizeof(uint32_t) * m,
+    e = hipMemcpy(visits.data(), p->last_set + kVisitsOffset, sizeof(uint32_t) * m,
                   hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy(visits)");
   }

@@ -143,10 +143,12 @@ __device__ __forceinline__ int32_t k_rotation_of(const KernelArgs &a, uint32_t i
 }
 
 // Thread 0 of every workgroup, once, after its last use of the run's scheduler
-// state: count the workgroup out; the last one of the grid resets the claim
-// counters, the gate and the count itself, so the next launch that uses this
-// state set (the plan's run after next, or the same launch replayed from a
-// graph) starts from zero without a host-side reset.
+// state, in runs that clean up after themselves (self_clean: launches captured
+// into a graph, which replay on one state set): count the workgroup out; the
+// last one of the grid resets the claim counters, the gate and the count
+// itself, so the next replay starts from zero without a host-side reset. Other
+// runs skip it: the plan's next run clears their set before it is used again
+// (the count's two dependent atomics at the end of a launch cost 2-4 us).
 // The count has two levels: a workgroup counts into its group (blockIdx mod
 // kExitGroups, one cache line per group), and the workgroup that completes a
 // group counts the group into exit_count; the one that completes the last
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
   const int32_t T = args.T;
 
   // ---- clear the next run's scheduler state (spread over the grid)
-  if (blockIdx.x == 0 && tid == 0) {
+  if (blockIdx.x == 0 && tid == 0 && args.ctrl_next != nullptr) {
     args.ctrl_next->counter = 0u;
     args.ctrl_next->gate = 0u;
     args.ctrl_next->error = 0u;
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     }
     __syncthreads();
     if (!gate_ok) {
-      if (tid == 0) leave_run(args);
+      if (tid == 0 && args.self_clean) leave_run(args);
       return;
     }
   }
@@ -1139,7 +1141,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
   if (tid == 0) {
     if (args.max_concurrent > 0)
       __hip_atomic_fetch_sub(&args.ctrl->gate, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    leave_run(args);
+    if (args.self_clean) leave_run(args);
   }
 }
 

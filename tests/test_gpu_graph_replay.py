@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import persistent_tiled_gemm_amd as ptg
-from tests.gpu_util import assert_close_rows, say, torch_mod, upload
+from tests.gpu_util import assert_close_rows, check_log, say, torch_mod, upload
 from workloads import make_problem
 
 pytestmark = pytest.mark.gpu
@@ -129,6 +129,45 @@ def test_grouped_run_replayed_from_a_graph(mode, order, policy):
             assert torch.equal(c, e), f"replay {i}: problem {j} differs from the eager run"
         other = other @ other.T / 512.0
         torch.cuda.synchronize()
+    del g
+    assert ptg.gemm_sync(plan, strict=False) == 0
+    plan.destroy()
+
+
+def test_replays_between_uncaptured_runs():
+    # a captured launch runs on the plan's graph state set; uncaptured runs of the
+    # same plan alternate between the two other sets and do not clean up after
+    # themselves. Replays and uncaptured runs in any order must all give the eager
+    # result (every mode, twice over, so that each uncaptured set is reused)
+    torch = torch_mod()
+    p = make_problem(1800, 1288, 520, "uniform", seed=83)   # 48 tiles, ragged edges and K tail
+    A, B = upload(p)
+    C = torch.full((p.M, p.N), float("nan"), dtype=torch.float32, device="cuda")
+    plan = ptg.gemm_create(tile_edge=256, log_capacity=1024)
+    ptg.gemm_run(A, B, C, plan, mode="dynamic")
+    ptg.gemm_sync(plan)
+    eager = C.clone()
+    assert_close_rows(p, eager.cpu().numpy(), [0, 255, 256, 1024, 1799])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ptg.gemm_run(A, B, C, plan, mode="dynamic", stream=s)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ptg.gemm_run(A, B, C, plan, mode="dynamic", stream=s)
+    for rnd in range(2):
+        for mode in MODES:
+            say(f"case replay between uncaptured runs round={rnd} mode={mode}")
+            C.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(C, eager), f"replay before the {mode} run differs"
+            C.fill_(float("nan"))
+            ptg.gemm_run(A, B, C, plan, mode=mode)
+            ptg.gemm_sync(plan)
+            assert torch.equal(C, eager), f"uncaptured {mode} run differs"
+            check_log(plan, mode, 48, P=ptg.gemm_plan_info_get(plan)["last_grid"] if mode == "static" else None)
     del g
     assert ptg.gemm_sync(plan, strict=False) == 0
     plan.destroy()
