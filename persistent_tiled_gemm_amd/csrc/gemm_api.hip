@@ -39,8 +39,9 @@ struct gemm_plan {
   int64_t wallclock_khz = 0;
   int lds_bytes = 0;
   int dyn_lds = 0;
-  // device scratch: two sets of [SchedCtrl][arrivals u32 x kMaxSplitTiles][visits u32 x
-  // log_capacity] followed by the sticky status word, plus the log and (tail
+  // device scratch: three sets of [SchedCtrl][arrivals u32 x kMaxSplitTiles][visits u32 x
+  // log_capacity] (two for uncaptured runs, one for captured launches) followed by
+  // the sticky status word, plus the log and (tail
   // splitting on) the partial-sum workspace
   unsigned char *d_ctrl_block = nullptr;
   uint32_t *d_status = nullptr;  // error bits of every run since the host last read them
