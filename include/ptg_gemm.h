@@ -257,9 +257,9 @@ typedef enum gemm_sched_mode {
  *                   many workgroups as can be resident at once (occupancy x CUs,
  *                   at most one per unit). Without launch cancel, the slots of
  *                   the full grid beyond the resident ones can only start as the
- *                   workers exit, and then leave again: about 2-3 us per launch
+ *                   workers exit, and then leave again: about 1-3 us per launch
  *                   of 1024 tiles with the per-XCD counters (each late slot
- *                   probes every region, then counts itself out). The schedule
+ *                   probes every region before it leaves). The schedule
  *                   is the same either way (the counters decide who takes which
  *                   unit).
  */
