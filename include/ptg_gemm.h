@@ -381,7 +381,7 @@ gemm_status gemm_run(const void *A, const void *B, float *C, int64_t M, int64_t 
  * gemm_run with the plan gemm_default_desc(256) gives (256 x 256 tiles,
  * per-XCD claim counters, one claim ahead, automatic K order, log off, no
  * split tail, no claim groups, no concurrency gate, B as K x N), with no plan: the scheduler state
- * lives in a library-owned device array of 4864 bytes per device (two control
+ * lives in a library-owned device array of 8960 bytes per device (two control
  * sets and a status word), which each device keeps until the process ends. Its
  * size does not depend on M, N or K; sizes beyond the library limits are
  * refused (GEMM_E_SHAPE) as by gemm_run. The first call on a device enqueues,

@@ -308,14 +308,14 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
 
 // ---- scratch of gemm_run_noalloc: the scheduler state in a file-scope device
 // array (each device holds its own copy until the process ends), so the entry
-// point never allocates. Layout: two control sets of 2304 bytes (the control
+// point never allocates. Layout: two control sets of 4352 bytes (the control
 // block: claim counters, gate, error word and the exit groups; run i uses set
 // i % 2 and clears the other for run i + 1, as a plan's sets do), then a
-// 256-byte status word block: 4864 bytes. The configuration is fixed (no log,
+// 256-byte status word block: 8960 bytes. The configuration is fixed (no log,
 // no split tail, no gate), so nothing in it grows with the problem.
 constexpr size_t kNoallocSetBytes = (sizeof(SchedCtrl) + 255) & ~(size_t)255;
 constexpr size_t kNoallocScratchBytes = 2 * kNoallocSetBytes + 256;
-static_assert(sizeof(SchedCtrl) <= kNoallocSetBytes && kNoallocScratchBytes == 4864, "control set");
+static_assert(sizeof(SchedCtrl) <= kNoallocSetBytes && kNoallocScratchBytes == 8960, "control set");
 static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 __global__ void ptg_zero_words(uint32_t *p, uint32_t n) {

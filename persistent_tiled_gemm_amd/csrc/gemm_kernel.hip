@@ -176,7 +176,7 @@ __device__ __forceinline__ void leave_run(const KernelArgs &a) {
     __hip_atomic_store(&a.ctrl->gate, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&a.ctrl->error, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int x = 0; x < kXcdRegions; ++x)
-      __hip_atomic_store(&a.ctrl->xcd_counter[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctrl->xcd_counter[(x) * kXcdStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int x = 0; x < kExitGroups; ++x)
       __hip_atomic_store(&a.ctrl->exit_group[x * kExitStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&a.ctrl->exit_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -259,7 +259,7 @@ __device__ __forceinline__ uint32_t region_unit(int policy, uint32_t T, uint32_t
   return y * q + (y < r ? y : r) + i;
 }
 __device__ __forceinline__ uint32_t claim_issue(const KernelArgs &a, uint32_t region) {
-  uint32_t *ctr = a.claim_policy == 0 ? &a.ctrl->counter : &a.ctrl->xcd_counter[region];
+  uint32_t *ctr = a.claim_policy == 0 ? &a.ctrl->counter : &a.ctrl->xcd_counter[(region) * kXcdStride];
   uint32_t v = 0;
   claim_issue_asm(ctr, true, v);
   return v;
@@ -275,14 +275,14 @@ __device__ __forceinline__ uint32_t claim_resolve(const KernelArgs &a, uint32_t 
   for (int attempt = 0; attempt < kXcdRegions; ++attempt) {
     bool open = false;
     if (lane < (uint32_t)kXcdRegions) {
-      const uint32_t seen = __hip_atomic_load(&a.ctrl->xcd_counter[my_y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t seen = __hip_atomic_load(&a.ctrl->xcd_counter[(my_y) * kXcdStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       open = seen < region_size(T, my_y);
     }
     const uint64_t mask = __ballot(open);
     if (mask == 0) return T;
     const uint32_t r = (uint32_t)__builtin_ctzll(mask);
     const uint32_t y = (xcc + r) % (uint32_t)kXcdRegions;
-    const uint32_t i = lane0_fetch_add(&a.ctrl->xcd_counter[y], lane);
+    const uint32_t i = lane0_fetch_add(&a.ctrl->xcd_counter[(y) * kXcdStride], lane);
     if (i < region_size(T, y)) {
       region = y;
       return region_unit(a.claim_policy, T, y, i);
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
     args.ctrl_next->gate = 0u;
     args.ctrl_next->error = 0u;
     args.ctrl_next->exit_count = 0u;
-    for (int x = 0; x < kXcdRegions; ++x) args.ctrl_next->xcd_counter[x] = 0u;
+    for (int x = 0; x < kXcdRegions; ++x) args.ctrl_next->xcd_counter[(x) * kXcdStride] = 0u;
     for (int x = 0; x < kExitGroups; ++x) args.ctrl_next->exit_group[x * kExitStride] = 0u;
   }
   if (args.clear_count > 0) {
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       bool open = false;
       if (args.claim_policy != 0) {
         if (lane < (uint32_t)kXcdRegions)
-          open = __hip_atomic_load(&args.ctrl->xcd_counter[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+          open = __hip_atomic_load(&args.ctrl->xcd_counter[(lane) * kXcdStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                  region_size((uint32_t)T, lane);
       } else if (lane == 0) {
         open = __hip_atomic_load(&args.ctrl->counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + args.counter_base <
@@ -763,7 +763,7 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
         wg_barrier();  // stage 0 read by every wave before step kb's loads refill it
         // claims are reserved now and sent between the two loop runs below
         if (claim_at >= 0) reserve_claims();
-        uint32_t *claim_ctr = args.claim_policy == 0 ? &args.ctrl->counter : &args.ctrl->xcd_counter[region];
+        uint32_t *claim_ctr = args.claim_policy == 0 ? &args.ctrl->counter : &args.ctrl->xcd_counter[(region) * kXcdStride];
         // The MFMA as a statement of its own, accumulating in place: each of the
         // 64 accumulators keeps one AGPR quad for the whole loop (all 256 AGPRs
         // hold accumulators, and with the builtin the register allocator
