@@ -238,6 +238,7 @@ gemm_status launch(gemm_plan *p, int32_t mode, bool grouped, KernelArgs &args, i
   if (mode == GEMM_SCHED_DYNAMIC && p->desc.dynamic_grid == GEMM_GRID_RESIDENT)
     grid = std::min<int64_t>(units, (int64_t)p->occupancy * p->cu_count);
   args.T = (int32_t)units;
+  args.first_wave = (int32_t)std::min<int64_t>(grid, (int64_t)p->occupancy * p->cu_count);
   args.items = (int32_t)items;
   args.claim_group = group;
   args.split_base = (int32_t)split_base;
@@ -579,6 +580,7 @@ gemm_status gemm_run_noalloc(const void *A, const void *B, float *C, int64_t M, 
   const int64_t workers = (int64_t)d->occupancy * d->cu_count;
   const int64_t grid = sched_mode == GEMM_SCHED_STATIC ? std::min<int64_t>(tiles, workers) : tiles;
   args.T = (int32_t)tiles;
+  args.first_wave = (int32_t)std::min<int64_t>(grid, workers);
   args.items = (int32_t)tiles;
   args.claim_group = 1;
   args.split_base = (int32_t)tiles;

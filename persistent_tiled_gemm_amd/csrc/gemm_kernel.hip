@@ -378,9 +378,15 @@ __global__ __launch_bounds__(TileCfg<BM>::type::THREADS, 1) void ptg_gemm_kernel
       // the thousands of late slots of a run with many small tiles sent their
       // atomics to the same counters as the last workers' final claims, whose
       // answers then came back many microseconds late (8192^3 with 128 x 128
-      // tiles: 845 -> 955 TFLOP/s)
+      // tiles: 845 -> 955 TFLOP/s). The slots of the first wave (the ones
+      // resident at launch) skip it: they start before any claim has gone out,
+      // so the counters are open, and the load would only delay their first
+      // claim by a round trip. (A first-wave slot that starts late claims
+      // anyway, as every slot did before the pre-check.)
       bool open = false;
-      if (args.claim_policy != 0) {
+      if (blockIdx.x < (uint32_t)args.first_wave) {
+        open = lane == 0;
+      } else if (args.claim_policy != 0) {
         if (lane < (uint32_t)kXcdRegions)
           open = __hip_atomic_load(&args.ctrl->xcd_counter[(lane) * kXcdStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                  region_size((uint32_t)T, lane);

@@ -97,6 +97,7 @@ struct KernelArgs {
   SchedCtrl *ctrl_next;         // the next run's set, cleared by this run
   uint32_t *clear_next;         // the next set's arrival + visit counters (contiguous)
   int32_t clear_count;          // counters to clear there
+  int32_t first_wave;           // dynamic: slots below this index claim without the pre-check (those resident at launch)
   int32_t self_clean;           // 1: the run leaves its set at zero when it ends (captured launches, which
                                 // replay on one set); 0: the next run clears the set instead
 };
