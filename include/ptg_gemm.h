@@ -41,8 +41,8 @@
  * blog post names splitting work along K as what removes this and leaves it out
  * of its design (first section); here it is the work-unit decomposition of a
  * run: the tiles that fill whole waves of workers stay whole units, and each
- * of the r = T mod P tiles of the partial last wave becomes S units, K-chunks
- * of nearly equal k-step counts. Every unit still has exactly one owner under
+ * of the r = T mod P tiles of the partial last wave (all T tiles when T < P)
+ * becomes S units, K-chunks of nearly equal k-step counts. Every unit still has exactly one owner under
  * every scheduler. A chunk writes its fp32 partial tile to plan scratch; the
  * workgroup that completes a tile's last chunk adds the S partials in chunk
  * order (a fixed order: results do not depend on which chunk finished last)
@@ -56,8 +56,8 @@
  *
  * Ownership. The caller owns A, B, C and keeps them alive until the stream has
  * passed the kernel. The plan (gemm_tile_cfg) owns all library scratch: the
- * claim counters, the tile log, the visit counters, the device status word and
- * the grouped-problem table. Runs are asynchronous and stream-ordered; nothing
+ * claim counters, the tile log, the visit counters, the device status word,
+ * the split tail's partial sums and the grouped-problem table. Runs are asynchronous and stream-ordered; nothing
  * here synchronises except gemm_sync, gemm_read_log, gemm_destroy and
  * gemm_test_spoiler's optional residency wait. Runs of one plan on different
  * streams are ordered on the device (a run waits for the plan's previous
