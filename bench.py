@@ -284,12 +284,15 @@ def run_tail_sections(ptg, torch, stream, khz, square):
         B = ptg.bf16_from_bits(q.b_bits)
         C = torch.empty((q.M, q.N), dtype=torch.float32, device="cuda")
         variants = {mode: (mode, plan) for mode in modes}
-        splan = None
+        splan = aplan = None
         if name == "tail_257":
-            # the one tile of the partial last wave split into (at most 4) K-chunks over idle workers
+            # the one tile of the partial last wave split into (at most 4) K-chunks over idle workers,
+            # and with the chunk count the library picks
             splan = ptg.gemm_create(tile_edge=256, log_capacity=512, tail_split=4)
+            aplan = ptg.gemm_create(tile_edge=256, log_capacity=512, tail_split=ptg.TAIL_SPLIT_AUTO)
             variants["static_tail_split"] = ("static", splan)
             variants["dynamic_tail_split"] = ("dynamic", splan)
+            variants["dynamic_tail_split_auto"] = ("dynamic", aplan)
         fns = {v: (lambda mode=mode, pl=pl: ptg.gemm_run(A, B, C, pl, mode=mode, stream=stream))
                for v, (mode, pl) in variants.items()}
         kernel_ms = time_interleaved(fns, rounds=4, per_round=5, stream=stream)
@@ -312,6 +315,7 @@ def run_tail_sections(ptg, torch, stream, khz, square):
             r[v] = ms
         if splan is not None:
             splan.destroy()
+            aplan.destroy()
         res[name] = r
         del A, B, C
     out["tail_boundary"] = res

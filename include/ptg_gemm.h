@@ -132,6 +132,7 @@ typedef enum gemm_sched_mode {
 #define GEMM_MAX_M (1 << 30)
 #define GEMM_MAX_TILES (1 << 30)
 #define GEMM_MAX_TAIL_SPLIT 64
+#define GEMM_TAIL_SPLIT_AUTO (-1) /* tail_split: the library picks the chunk count per run */
 #define GEMM_MAX_CLAIM_GROUP 16
 
 /*
@@ -187,7 +188,12 @@ typedef enum gemm_sched_mode {
  *                   from C; in the dynamic mode the other workers claim them.
  *   max_groups      capacity of the grouped-problem table (0 = 1024).
  *   device          HIP device ordinal; must be gfx950.
- *   tail_split      0 = off. s in 2..GEMM_MAX_TAIL_SPLIT: split each tile of a
+ *   tail_split      0 = off. GEMM_TAIL_SPLIT_AUTO (-1): split as below with a
+ *                   chunk count the library picks per run: the largest power
+ *                   of two up to 8 that gives every chunk an idle CU and at
+ *                   least 64 k-steps (16 when fewer than 32 tiles split; four
+ *                   times that for 128 x 128 tiles), 1 (no split) if none.
+ *                   s in 2..GEMM_MAX_TAIL_SPLIT: split each tile of a
  *                   partial last wave into at most s K-chunks (fewer when the
  *                   idle workers or K, at >= 8 k-steps of bk a chunk, allow
  *                   fewer). Workers per wave: the static mode's P, else

@@ -42,7 +42,7 @@ from typing import Dict, Iterable, List, Optional
 
 import numpy as np
 
-__all__ = ["check_ownership", "check_k_cover", "split_units", "makespan", "per_worker", "region_of"]
+__all__ = ["check_ownership", "check_k_cover", "split_units", "auto_split_chunks", "makespan", "per_worker", "region_of"]
 
 
 def per_worker(worker: np.ndarray, tiles: np.ndarray) -> Dict[int, np.ndarray]:
@@ -175,6 +175,24 @@ def check_k_cover(tile: np.ndarray, k_begin: np.ndarray, k_end: np.ndarray, T: i
             if pos != int(Ks[t]):
                 errs.append(f"tile {t}: K covered up to {pos}, not {int(Ks[t])}")
     return errs
+
+
+def auto_split_chunks(r: int, nk: int, cus: int, tile_edge: int = 256) -> int:
+    """Chunk count S of the automatic split for r split tiles of nk k-steps on cus
+    compute units. A rule of this implementation (the pages only name splitting
+    along K as the cure for quantisation): the largest power of two S <= 8 such
+    that every chunk gets an idle CU (r S <= cus) and at least min_steps k-steps,
+    min_steps = 64 when 32 or more tiles split at once and 16 when fewer, times 4
+    for 128 x 128 tiles; 1 (no split) when no S >= 2 qualifies.
+    """
+    if r <= 0:
+        return 1
+    min_steps = (64 if r >= 32 else 16) * (4 if tile_edge == 128 else 1)
+    best = 1
+    for S in (2, 4, 8):
+        if r * S <= cus and nk // S >= min_steps:
+            best = S
+    return best
 
 
 def split_units(T: int, workers: int, nk: int, max_chunks: int, min_chunk_steps: int = 4,

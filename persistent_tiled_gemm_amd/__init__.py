@@ -32,6 +32,7 @@ MODES = {"nonpersistent": SCHED_NONPERSISTENT, "static": SCHED_STATIC, "dynamic"
 # K orders (plan field k_rotation)
 KROT_AUTO, KROT_OFF, KROT_XCD, KROT_XCD2, KROT_UNIT = 0, 1, 2, 3, 4
 GRID_ALL, GRID_RESIDENT = 0, 1  # gemm_tile_desc.dynamic_grid
+TAIL_SPLIT_AUTO = -1  # gemm_tile_desc.tail_split: the library picks the chunk count per run
 
 GEMM_OK = 0
 STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_E_INVALID_ARG", -2: "GEMM_E_SHAPE", -3: "GEMM_E_UNSUPPORTED",

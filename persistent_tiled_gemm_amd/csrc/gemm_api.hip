@@ -191,6 +191,28 @@ constexpr uint32_t kDefaultGateSpinLimit = 1u << 22;
 // Fewest k-steps (of bk = 32) a K-chunk of a split tile gets.
 constexpr int64_t kMinChunkSteps = 8;
 
+// Chunk count of tail_split = GEMM_TAIL_SPLIT_AUTO for r split tiles of nk
+// k-steps on `cus` compute units: the largest power of two up to 8 such that
+// every chunk has an idle CU of its own (r S <= cus) and at least min_steps
+// k-steps. A chunk's partial sum costs its tile a fix-up (one workgroup reads
+// the S partials and writes the tile, 20-35 us for a 256 x 256 tile split four
+// ways when 32-64 tiles fix up at once), so chunks must be long when many
+// tiles split at once (64 k-steps from 32 split tiles on) and may be short
+// when few do (16); 128 x 128 tiles carry a quarter of the work per k-step,
+// so their chunks need four times the steps. Chosen from measurements on
+// MI355X (256 x 256 tiles, dynamic, us, whole -> split): 2048^2 x 8192 (64
+// tiles) 140 -> 98 at S = 4; 2048^2 x 4096 78 -> 64 at S = 2; 2048^2 x 2048
+// 48, no split; 512^2 x 16384 (4 tiles) 255 -> 70 at S = 8; 257 tiles of
+// 256 x 256 x 4096 205 -> 168 at S = 4 or 8.
+int64_t auto_split_chunks(int64_t r, int64_t nk, int64_t cus, int32_t tile_edge) {
+  if (r <= 0) return 1;
+  const int64_t min_steps = (r >= 32 ? 64 : 16) * (tile_edge == 128 ? 4 : 1);
+  const int64_t bound = std::min<int64_t>({8, cus / r, nk / min_steps});
+  int64_t S = 1;
+  while (S * 2 <= bound) S *= 2;
+  return S;
+}
+
 // Work items of a run: T whole tiles, or, with tail splitting on, the tiles
 // that fill whole waves of `workers` plus the r = T mod workers tiles of the
 // partial last wave, each split into S K-chunks (S <= tail_split, <= workers / r
@@ -208,14 +230,18 @@ void plan_units(const gemm_plan *p, bool grouped, int32_t mode, int64_t tiles, i
     *group = p->desc.claim_group;
     return;
   }
-  if (grouped || p->desc.tail_split < 2 || p->ws_tiles == 0) return;
+  const bool auto_split = p->desc.tail_split == GEMM_TAIL_SPLIT_AUTO;
+  if (grouped || (!auto_split && p->desc.tail_split < 2) || p->ws_tiles == 0) return;
   const int64_t workers =
       mode == GEMM_SCHED_STATIC ? (int64_t)p->static_workers : (int64_t)p->occupancy * p->cu_count;
   if (workers < 2) return;
   const int64_t r = tiles % workers;
   if (r == 0 || r > ptg::kMaxSplitTiles) return;
   const int64_t nk = ceil_div(K, p->desc.bk);
-  const int64_t S = std::min<int64_t>({(int64_t)p->desc.tail_split, workers / r, nk / kMinChunkSteps, p->ws_tiles / r});
+  const int64_t S =
+      auto_split ? std::min<int64_t>(auto_split_chunks(r, nk, std::max<int64_t>(1, workers / p->occupancy), p->desc.bm),
+                                     p->ws_tiles / r)
+                 : std::min<int64_t>({(int64_t)p->desc.tail_split, workers / r, nk / kMinChunkSteps, p->ws_tiles / r});
   if (S < 2) return;
   *split_base = tiles - r;
   *chunks = (int32_t)S;
@@ -420,7 +446,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
   if (d.claim_lead < 0 || d.claim_policy < 0 || d.claim_policy > 2) return GEMM_E_INVALID_ARG;
   if (d.raster < 0 || d.raster > 1 || (d.raster == 1 && d.raster_group < 1)) return GEMM_E_INVALID_ARG;
   if (d.static_workers < 0 || d.log_capacity < 0 || d.min_lds_bytes < 0 || d.max_concurrent < 0 ||
-      d.max_groups < 0 || d.tail_split < 0 || d.tail_split > GEMM_MAX_TAIL_SPLIT || d.group_order < 0 ||
+      d.max_groups < 0 || d.tail_split < GEMM_TAIL_SPLIT_AUTO || d.tail_split > GEMM_MAX_TAIL_SPLIT || d.group_order < 0 ||
       d.group_order > 1 || d.claim_group < 0 || d.claim_group > GEMM_MAX_CLAIM_GROUP || d.b_layout < 0 ||
       d.b_layout > 1 || d.gate_spin_limit < 0 || d.k_rotation < GEMM_KROT_AUTO || d.k_rotation > GEMM_KROT_UNIT ||
       d.dynamic_grid < GEMM_GRID_ALL || d.dynamic_grid > GEMM_GRID_RESIDENT)
@@ -478,7 +504,7 @@ gemm_status gemm_create(gemm_tile_cfg *out, const gemm_tile_desc *desc) {
       return GEMM_E_NOMEM;
     }
   }
-  if (d.tail_split >= 2) {
+  if (d.tail_split >= 2 || d.tail_split == GEMM_TAIL_SPLIT_AUTO) {
     // the K-chunks of one run never outnumber the workers of one wave
     p->ws_tiles = std::max<int64_t>((int64_t)occ * p->cu_count, p->static_workers);
     if (hipMalloc(&p->d_ws, sizeof(float) * (size_t)d.bm * (size_t)d.bn * (size_t)p->ws_tiles) != hipSuccess) {

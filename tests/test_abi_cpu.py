@@ -59,7 +59,8 @@ def test_status_strings_and_defaults(lib):
 
 
 def test_descriptor_values_out_of_range_are_rejected_before_any_hip_call(lib):
-    for field, bad in (("dynamic_grid", 2), ("dynamic_grid", -1), ("k_rotation", 5), ("claim_policy", 3)):
+    for field, bad in (("dynamic_grid", 2), ("dynamic_grid", -1), ("k_rotation", 5), ("claim_policy", 3),
+                       ("tail_split", -2), ("tail_split", 65)):
         d = ptg.gemm_default_desc(256, 0)
         setattr(d, field, bad)
         out = ctypes.c_void_p()

@@ -170,3 +170,35 @@ def test_tail_split_underfilled_grid(tile, shape):
     assert np.array_equal(outs["static"], outs["dynamic"])
     assert np.array_equal(outs["nonpersistent"], outs["dynamic"])
     plan.destroy()
+
+
+@pytest.mark.parametrize("tile,shape", [(256, (2048, 2048, 8192)), (256, (2048, 2048, 2048)), (256, (257 * 256, 256, 4096)),
+                                        (256, (512, 512, 16384)), (128, (300, 264, 16384)), (128, (1000, 776, 2056))])
+def test_tail_split_auto(tile, shape):
+    """tail_split = TAIL_SPLIT_AUTO: the run's chunk count is oracle.ownership.auto_split_chunks
+    of its partial wave (1 = whole tiles), the units are split_units' with that count, and C
+    matches the oracle; static and dynamic give the same bits."""
+    from oracle.ownership import auto_split_chunks
+    M, N, K = shape
+    p = make_problem(M, N, K, "uniform", seed=M + K)
+    plan = make_plan(tile, tail_split=ptg.TAIL_SPLIT_AUTO, log_capacity=4096)
+    info = ptg.gemm_plan_info_get(plan)
+    workers = info["occupancy"] * info["cu_count"]
+    tn = -(-N // tile)
+    T = -(-M // tile) * tn
+    r = T % workers
+    S = auto_split_chunks(r, -(-K // 32), info["cu_count"], tile)
+    want_items = T - r + r * S if S > 1 else T
+    outs = {}
+    for mode in ("static", "dynamic"):
+        say(f"case tail split auto tile={tile} shape={shape} mode={mode} (r={r}, S={S})")
+        c = run(p, plan, mode)
+        info = ptg.gemm_plan_info_get(plan)
+        assert info["last_split_chunks"] == S and info["last_items"] == want_items, info
+        log = check_log(plan, mode, want_items, P=info["last_grid"] if mode == "static" else None, K=K, tiles=T)
+        want = _expect_units(plan, log, T, workers, K, S)
+        rows = sorted(set(_split_rows(want, tile, M, tn)[::3]) | {0, M // 2, M - 1}) if S > 1 else [0, 1, M // 2, M - 1]
+        assert_close_rows(p, c, rows)
+        outs[mode] = c
+    assert np.array_equal(outs["static"], outs["dynamic"])
+    plan.destroy()

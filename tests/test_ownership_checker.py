@@ -134,3 +134,28 @@ def test_split_units_decomposition():
         t = np.array([x[0] for x in u]); b = np.array([x[1] for x in u]); e = np.array([x[2] for x in u])
         assert check_k_cover(t, b, e, T, nk) == []
         assert all(x[2] - x[1] >= 4 for x in u if x[2] - x[1] != nk)
+
+
+def test_auto_split_chunks_is_the_largest_qualifying_power_of_two():
+    """The automatic chunk count against its definition, checked by an independent
+    search over every S in 1..8 on a grid of (r, nk, cus, tile edge), and at the
+    design points measured on the part (whole tiles against S = 2 / 4 / 8)."""
+    from oracle.ownership import auto_split_chunks
+    for tile in (128, 256):
+        for cus in (8, 64, 256):
+            for r in (1, 2, 3, 7, 31, 32, 33, 64, 100, 256):
+                for nk in (1, 15, 16, 31, 32, 63, 64, 65, 127, 128, 255, 256, 512, 1024, 4096):
+                    S = auto_split_chunks(r, nk, cus, tile)
+                    need = (64 if r >= 32 else 16) * (4 if tile == 128 else 1)
+                    ok = [s for s in range(1, 9) if s & (s - 1) == 0 and (s == 1 or (r * s <= cus and nk // s >= need))]
+                    assert S == max(ok), (tile, cus, r, nk, S, ok)
+    assert auto_split_chunks(0, 256, 256) == 1
+    # measured on MI355X (256 x 256 tiles unless stated; the best of whole / 2 / 4 / 8 chunks)
+    assert auto_split_chunks(64, 256, 256) == 4          # 2048 x 2048 x 8192: 140 -> 98 us
+    assert auto_split_chunks(64, 128, 256) == 2          # 2048 x 2048 x 4096: 78 -> 64 us
+    assert auto_split_chunks(64, 64, 256) == 1           # 2048 x 2048 x 2048: no split pays
+    assert auto_split_chunks(4, 512, 256) == 8           # 512 x 512 x 16384: 255 -> 70 us
+    assert auto_split_chunks(32, 256, 256) == 4          # 8448 x 8192 x 8192 (32 tail tiles): 838 -> 794 us
+    assert auto_split_chunks(1, 128, 256) == 8           # the 257-tile tail boundary: 205 -> 168 us
+    assert auto_split_chunks(256, 256, 256, 128) == 1    # 2048 x 2048 x 8192 in 128 x 128 tiles: splitting lost
+    assert auto_split_chunks(64, 256, 256, 128) == 1     # 1024 x 1024 x 8192 in 128 x 128 tiles: 4 chunks lost
