@@ -1,5 +1,5 @@
 """GPU parity at the full sizes of the measured workloads, in the launch
-configuration the benchmark times (256x256x64 tiles, claims-ahead 1, ring depth
+configuration the benchmark times (256 x 256 tiles in 32-deep k-steps, claims-ahead 1, ring depth
 3, tile log on). Outputs are checked against the oracle on sampled rows (the
 oracle computes them row by row); ownership is checked bit-exactly on the log.
 """
